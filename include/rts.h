@@ -1,0 +1,143 @@
+/*
+ * rts.h -- C ABI of the MI355X (gfx950) per-token sampler.
+ *
+ * For each of B rows of fp32 head logits the library runs the sampling chain
+ * of page "#19 serve: per-request temperature/top_p/top_k/min_p/penalties
+ * sampling" (section "What changed"):
+ *   penalties (repeat / frequency / presence over a history window, looked up
+ *   through a per-chunk token bitmap) -> top_k (k in 1..64, kept in
+ *   descending order, ties to the lowest index) -> min_p cut -> top_p cut ->
+ *   temperature -> Philox4x32-10 draw keyed by (seed, counter);
+ * and the logprobs of page "#3200 [Engine] OpenAI logprobs / top_logprobs /
+ * allowed_token_ids for the CUDA/HIP engine" (sections "Problem and result",
+ * "Approach", "Limits"): log-softmax of the raw logits with up to 20 top
+ * entries, optionally renormalised over a list of allowed ids.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory; "host" are host memory
+ *    read before the call returns.  The caller owns every buffer; the library
+ *    allocates nothing and keeps no pointer after returning.
+ *  - Work is enqueued on `stream` and runs asynchronously; outputs are valid
+ *    once the stream has reached that point.  A workspace may not be used by
+ *    two calls that can run at the same time.
+ *  - Return value: RTS_OK, or a negative RTS_E* code.  All argument checks
+ *    run before anything is enqueued, so a failed call writes nothing.
+ *    rts_last_error() names the offending row and field (per thread).
+ *  - Device-resident ids (history rows, allowed lists, tokens) are not
+ *    validated: ids outside [0, V) are ignored as the pages' semantics
+ *    require no host round trip.
+ */
+#ifndef RTS_H
+#define RTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RTS_OK 0
+#define RTS_EINVAL (-1)  /* a bad shape, pointer or per-row parameter   */
+#define RTS_ENOSPC (-2)  /* the workspace is smaller than required      */
+#define RTS_EDEVICE (-3) /* a HIP launch error                          */
+
+#define RTS_MAX_TOP_K 64 /* top_k limit of sampled rows (#19, "A persistent per-request draw counter") */
+#define RTS_KEPT 64      /* entries per row of kept_ids / kept_logits          */
+#define RTS_MAX_TOP_N 20 /* top_logprobs limit (#3200, "Problem and result")   */
+#define RTS_MAX_WINDOW 65535 /* longest penalty window, in ids                  */
+
+/*
+ * Per-row request (#19, "What changed": the per-request paragraph lists the
+ * keys; the counter paragraph makes the counter the caller's).  56 bytes.
+ */
+typedef struct rts_row_params {
+    float temperature;     /* <= 0: greedy (argmax of the penalised logits); else finite > 0 */
+    int32_t top_k;         /* sampled rows: 1..64, else RTS_EINVAL; ignored for greedy rows  */
+    float top_p;           /* (0, 1]; 1 disables the cut                                     */
+    float min_p;           /* [0, 1]; 0 disables the cut                                     */
+    float penalty_repeat;  /* finite > 0; 1 = neutral                                        */
+    float penalty_freq;    /* finite; 0 = neutral                                            */
+    float penalty_present; /* finite; 0 = neutral                                            */
+    int32_t penalty_last_n;/* -1: whole history row, 0: no penalties, > 0: window length     */
+    int32_t history_row;   /* -1: none (neutral path), else a row index into `history`       */
+    int32_t reserved;      /* must be 0                                                      */
+    uint64_t seed;         /* Philox key (low word, high word)                               */
+    uint64_t counter;      /* Philox counter (low word, high word, 0, 0); caller-owned       */
+} rts_row_params;
+
+/* Bytes of workspace that calls with up to B rows of V logits need
+ * (both entry points).  *bytes is set on RTS_OK. */
+int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes);
+
+/* Prepare a fresh workspace (zero its counters) on `stream`.  A workspace
+ * that was zero-filled by the caller needs no call; the library returns its
+ * counters to zero at the end of every call. */
+int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The sampling chain over B rows.
+ *   logits      device fp32 [B][ld], row-major, ld >= V; 0 < V < 2^31.
+ *   params      host [B].
+ *   history     device int32 [H][ldh] or NULL when no row names one; row h
+ *               holds history_len[h] ids, oldest first.  The window of a row
+ *               is the last min(penalty_last_n, history_len) ids of its
+ *               history row (all of them for penalty_last_n = -1), at most
+ *               RTS_MAX_WINDOW ids.  Rows of a verify window may share one
+ *               history row (#19, "What changed", the penalties paragraph).
+ *   history_len host int32 [H].
+ * Outputs (device; all but `token` may be NULL):
+ *   token       int32 [B]      the sampled id (greedy: the argmax).
+ *   counts      int32 [B][3]   (k_eff, kept after min_p, kept after top_p).
+ *   kept_ids    int32 [B][64]  the top_k sequence, padded with -1.
+ *   kept_logits f32 [B][64]    its penalised logits, padded with -inf.
+ *   philox_x0   uint32 [B]     first Philox output word (0 for greedy rows).
+ * Errors: RTS_EINVAL for B < 0, V out of range, ld < V, NULL logits/token,
+ * a row with NaN or infinite temperature, top_k outside 1..64 on a sampled
+ * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
+ * non-finite penalties, history_row >= H or set without history, a window
+ * longer than RTS_MAX_WINDOW, or reserved != 0; RTS_ENOSPC for a short
+ * workspace; RTS_EDEVICE if a launch fails.  B = 0 is a no-op.
+ */
+int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
+                      const rts_row_params *params,
+                      const int32_t *history, int64_t H, int64_t ldh,
+                      const int32_t *history_len,
+                      int32_t *token, int32_t *counts, int32_t *kept_ids,
+                      float *kept_logits, uint32_t *philox_x0,
+                      void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Log-softmax of the raw logits (before penalties and temperature), per row.
+ *   logits      device fp32 [B][ld] as above; NaN counts as -inf, +inf as
+ *               the largest finite float.
+ *   tokens      device int32 [B]: the ids whose logprob is reported.
+ *   top_n       0..20 entries of top_ids / top_lp per row.
+ *   allowed     device int32 ids, row r owning allowed[allowed_off[r] ..
+ *               allowed_off[r+1]); NULL for no restriction.  A row with an
+ *               empty range is unrestricted; duplicates count once; ids
+ *               outside [0, V) are ignored.  Restricted rows need V <= 2^19.
+ *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] = 0.
+ * Outputs (device): token_lp f32 [B] (-inf when the token is outside the
+ * row's domain), top_ids int32 [B][top_n] and top_lp f32 [B][top_n], the
+ * domain's largest logits in (logit desc, index asc) order, padded with
+ * (-1, -inf).  top_ids/top_lp may be NULL when top_n = 0.
+ */
+int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
+                       const int32_t *tokens, int32_t top_n,
+                       const int32_t *allowed, const int64_t *allowed_off,
+                       float *token_lp, int32_t *top_ids, float *top_lp,
+                       void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of an error code. */
+const char *rts_strerror(int code);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *rts_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

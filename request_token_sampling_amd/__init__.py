@@ -1,0 +1,217 @@
+"""Per-token sampling chain and raw-logit logprobs on MI355X (gfx950).
+
+A thin ctypes binding of the C ABI in include/rts.h (librts.so, built in-tree
+by ``python -m request_token_sampling_amd.build_lib``).  It only marshals
+arguments: torch provides device memory and the current stream, every step of
+the chain runs in the library's HIP kernels, and the library itself checks
+every argument.  There is no CPU fallback: if the library is missing, import
+of the entry points fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librts.so")
+
+RTS_OK, RTS_EINVAL, RTS_ENOSPC, RTS_EDEVICE = 0, -1, -2, -3
+MAX_TOP_K = 64
+KEPT = 64
+MAX_TOP_N = 20
+
+
+class RTSError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"rts error {code}: {msg}")
+        self.code = code
+
+
+class RowParams(ctypes.Structure):
+    """Mirror of rts_row_params (56 bytes)."""
+    _fields_ = [
+        ("temperature", ctypes.c_float),
+        ("top_k", ctypes.c_int32),
+        ("top_p", ctypes.c_float),
+        ("min_p", ctypes.c_float),
+        ("penalty_repeat", ctypes.c_float),
+        ("penalty_freq", ctypes.c_float),
+        ("penalty_present", ctypes.c_float),
+        ("penalty_last_n", ctypes.c_int32),
+        ("history_row", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+        ("counter", ctypes.c_uint64),
+    ]
+
+
+assert ctypes.sizeof(RowParams) == 56
+
+_DEFAULTS = dict(temperature=0.0, top_k=0, top_p=1.0, min_p=0.0, penalty_repeat=1.0,
+                 penalty_freq=0.0, penalty_present=0.0, penalty_last_n=0, history_row=-1,
+                 reserved=0, seed=0, counter=0)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librts.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "python -m request_token_sampling_amd.build_lib")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.rts_workspace_bytes.argtypes = [I64, I64, ctypes.POINTER(ctypes.c_size_t)]
+        L.rts_workspace_init.argtypes = [P, SZ, P]
+        L.rts_sample_tokens.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P, P, P,
+                                        SZ, P]
+        L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
+        for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
+                  "rts_token_logprobs"):
+            getattr(L, f).restype = ctypes.c_int
+        L.rts_strerror.argtypes = [ctypes.c_int]
+        L.rts_strerror.restype = ctypes.c_char_p
+        L.rts_last_error.argtypes = []
+        L.rts_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != RTS_OK:
+        msg = lib().rts_last_error().decode() or lib().rts_strerror(rc).decode()
+        raise RTSError(rc, msg)
+
+
+def row_params(rows) -> ctypes.Array:
+    """A list of dicts (missing keys neutral) -> rts_row_params[B]."""
+    arr = (RowParams * max(len(rows), 1))()
+    for i, d in enumerate(rows):
+        full = dict(_DEFAULTS)
+        full.update(d)
+        for k, v in full.items():
+            setattr(arr[i], k, v)
+    return arr
+
+
+def workspace_bytes(B: int, V: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().rts_workspace_bytes(B, V, ctypes.byref(n)))
+    return int(n.value)
+
+
+def make_workspace(B: int, V: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace (zero counters need no rts_workspace_init)."""
+    return torch.zeros(workspace_bytes(B, V), dtype=torch.uint8, device=device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows_view(logits: torch.Tensor):
+    if logits.dim() == 1:
+        logits = logits.unsqueeze(0)
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda:
+        raise ValueError("logits must be a 2-D float32 CUDA tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    B, V = logits.shape
+    return logits, B, V, logits.stride(0) if B > 1 else V
+
+
+class SampleCall:
+    """One prepared call of rts_sample_tokens: outputs, workspace and ctypes
+    arguments are built once, so repeated calls (benchmarks, decode loops over
+    fixed buffers) pay only the C call.  Params may be replaced between calls
+    with ``set_params``."""
+
+    def __init__(self, logits, params, history=None, history_len=None, workspace=None,
+                 stream=None):
+        self.logits, self.B, self.V, self.ld = _rows_view(logits)
+        dev = self.logits.device
+        self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.counts = torch.empty((self.B, 3), dtype=torch.int32, device=dev)
+        self.kept_ids = torch.empty((self.B, KEPT), dtype=torch.int32, device=dev)
+        self.kept_logits = torch.empty((self.B, KEPT), dtype=torch.float32, device=dev)
+        self.philox_x0 = torch.empty(self.B, dtype=torch.int32, device=dev)
+        self.workspace = workspace if workspace is not None else make_workspace(self.B, self.V, dev)
+        self.history = history
+        if history is not None:
+            if history.dtype != torch.int32 or history.dim() != 2 or history.stride(1) != 1:
+                raise ValueError("history must be a 2-D int32 tensor with contiguous rows")
+            self.H, self.ldh = history.shape[0], history.stride(0)
+            self.hist_len = np.ascontiguousarray(history_len, dtype=np.int32)
+        else:
+            self.H, self.ldh, self.hist_len = 0, 0, None
+        self.set_params(params)
+        self.stream = stream
+
+    def set_params(self, params):
+        self.params = params if isinstance(params, ctypes.Array) else row_params(params)
+
+    def __call__(self):
+        L = lib()
+        rc = L.rts_sample_tokens(
+            _ptr(self.logits), self.B, self.V, self.ld, self.params,
+            _ptr(self.history), self.H, self.ldh,
+            None if self.hist_len is None else self.hist_len.ctypes.data_as(ctypes.c_void_p),
+            _ptr(self.token), _ptr(self.counts), _ptr(self.kept_ids), _ptr(self.kept_logits),
+            _ptr(self.philox_x0), _ptr(self.workspace), self.workspace.numel(),
+            _stream_handle(self.stream))
+        _check(rc)
+        return self
+
+    def results(self) -> dict:
+        """Device tensors; philox_x0 holds the uint32 words' bits as int32."""
+        return dict(token=self.token, counts=self.counts, kept_ids=self.kept_ids,
+                    kept_logits=self.kept_logits, philox_x0=self.philox_x0)
+
+
+def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
+                  stream=None) -> dict:
+    """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
+
+    params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
+    history: CUDA int32 [H][ldh] with host lengths history_len[H], or None.
+    Returns device tensors token[B], counts[B][3], kept_ids[B][64],
+    kept_logits[B][64], philox_x0[B]."""
+    return SampleCall(logits, params, history, history_len, workspace, stream)().results()
+
+
+def token_logprobs(logits, tokens, top_n: int, allowed=None, allowed_off=None,
+                   workspace=None, stream=None) -> dict:
+    """Raw-logit log-softmax per row: token_lp[B], top_ids[B][top_n],
+    top_lp[B][top_n].  allowed: CUDA int32 ids with host int64 offsets [B+1]."""
+    logits, B, V, ld = _rows_view(logits)
+    dev = logits.device
+    if tokens.dtype != torch.int32 or not tokens.is_cuda:
+        raise ValueError("tokens must be a CUDA int32 tensor")
+    token_lp = torch.empty(B, dtype=torch.float32, device=dev)
+    top_ids = torch.empty((B, max(top_n, 0)), dtype=torch.int32, device=dev)
+    top_lp = torch.empty((B, max(top_n, 0)), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else make_workspace(B, V, dev)
+    off = None
+    if allowed is not None:
+        off = np.ascontiguousarray(allowed_off, dtype=np.int64)
+    rc = lib().rts_token_logprobs(
+        _ptr(logits), B, V, ld, _ptr(tokens), int(top_n),
+        _ptr(allowed), None if off is None else off.ctypes.data_as(ctypes.c_void_p),
+        _ptr(token_lp), _ptr(top_ids) if top_n > 0 else None,
+        _ptr(top_lp) if top_n > 0 else None, _ptr(ws), ws.numel(), _stream_handle(stream))
+    _check(rc)
+    return dict(token_lp=token_lp, top_ids=top_ids, top_lp=top_lp)
+
+
+__all__ = ["sample_tokens", "token_logprobs", "SampleCall", "workspace_bytes",
+           "make_workspace", "row_params", "RowParams", "RTSError", "lib"]

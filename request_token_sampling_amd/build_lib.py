@@ -1,0 +1,44 @@
+"""Build of the HIP library librts.so (gfx950), in-tree next to this file.
+
+Run ``python -m request_token_sampling_amd.build_lib``.  Compiles every time
+it is called.  Flags: -ffp-contract=off keeps the penalty arithmetic at one
+rounding per operation; packed fp32 instructions are disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "librts.so")
+SOURCES = ["rts_api.cpp", "rts_sample.hip", "rts_logprobs.hip"]
+ARCH = os.environ.get("RTS_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc_cmd(out: str, extra=()) -> list:
+    return ["/opt/rocm/bin/hipcc", "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC",
+            "-shared", "-ffp-contract=off", "-fno-fast-math",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function",
+            "-I", INCLUDE, "-I", CSRC, *extra, "-o", out,
+            *[os.path.join(CSRC, s) for s in SOURCES],
+            "-Wl,-rpath,/opt/rocm/lib"]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = hipcc_cmd(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

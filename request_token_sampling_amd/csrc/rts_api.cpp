@@ -1,0 +1,331 @@
+// rts_api.cpp -- the C ABI declared in include/rts.h: argument checks, the
+// per-launch argument blocks, chunk sizing and the launches.  Every check
+// runs before anything is enqueued, so a refused call writes nothing (page
+// "#19 serve: per-request temperature/top_p/top_k/min_p/penalties sampling",
+// "What changed": a sampled request outside top_k 1..64 is refused rather
+// than left to write a stale token, and a bad sampling value is refused
+// rather than silently changed).
+#include "rts.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rts_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+// Rows per launch and elements per thread.  A launch covers up to 64 rows;
+// each workgroup covers a chunk of 256 * ept elements.  The chunk is the
+// largest whose grid still has >= 512 workgroups (two per CU), so a batch of
+// long rows streams in big chunks and a single row still spreads over the
+// chip; the smallest chunk is 1024 elements.
+int choose_ept(int64_t rows, int64_t V)
+{
+    static const int opts[4] = {32, 16, 8, 4};
+    for (int i = 0; i < 4; ++i) {
+        const int64_t ch = (int64_t)rts::kBlock * opts[i];
+        const int64_t nch = (V + ch - 1) / ch;
+        if (rows * nch >= 512) return opts[i];
+    }
+    return 4;
+}
+
+int64_t chunks_for(int64_t V, int ept)
+{
+    const int64_t ch = (int64_t)rts::kBlock * ept;
+    return (V + ch - 1) / ch;
+}
+
+bool is_vec_ok(const float *p, int64_t ld)
+{
+    return (reinterpret_cast<uintptr_t>(p) % 16u) == 0u && (ld % 4) == 0;
+}
+
+size_t max_lds_per_block()
+{
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 65536;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return 65536;
+    return (size_t)v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rts_strerror(int code)
+{
+    switch (code) {
+    case RTS_OK: return "ok";
+    case RTS_EINVAL: return "invalid argument";
+    case RTS_ENOSPC: return "workspace too small";
+    case RTS_EDEVICE: return "HIP launch error";
+    default: return "unknown error";
+    }
+}
+
+const char *rts_last_error(void) { return g_last_error; }
+
+int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes)
+{
+    clear_error();
+    if (bytes == nullptr) return fail(RTS_EINVAL, "bytes is NULL");
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    const int64_t rows = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
+    const size_t per_row = rts::keys_bytes_per_row(V) + rts::partial_bytes_per_row(V);
+    size_t total = rts::kTicketBytes + (size_t)(rows > 0 ? rows : 1) * per_row;
+    total = (total + 255u) & ~(size_t)255u;
+    *bytes = total;
+    return RTS_OK;
+}
+
+int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
+    if (ws_bytes < rts::kTicketBytes) return fail(RTS_ENOSPC, "workspace of %zu bytes", ws_bytes);
+    const int e = rts::launch_zero_u32(static_cast<uint32_t *>(workspace),
+                                       rts::kTicketBytes / 4u, stream);
+    if (e != 0) return fail(RTS_EDEVICE, "zero kernel: %s", hipGetErrorString((hipError_t)e));
+    return RTS_OK;
+}
+
+int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
+                      const rts_row_params *params,
+                      const int32_t *history, int64_t H, int64_t ldh,
+                      const int32_t *history_len,
+                      int32_t *token, int32_t *counts, int32_t *kept_ids,
+                      float *kept_logits, uint32_t *philox_x0,
+                      void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (B == 0) return RTS_OK;
+    if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
+    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
+    if (logits == nullptr) return fail(RTS_EINVAL, "logits is NULL");
+    if (params == nullptr) return fail(RTS_EINVAL, "params is NULL");
+    if (token == nullptr) return fail(RTS_EINVAL, "token is NULL");
+    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
+    if (H < 0 || ldh < 0) return fail(RTS_EINVAL, "H = %lld, ldh = %lld", (long long)H, (long long)ldh);
+    size_t need = 0;
+    rts_workspace_bytes(B, V, &need);
+    if (ws_bytes < need)
+        return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+
+    // Check every row before enqueuing anything.
+    for (int64_t r = 0; r < B; ++r) {
+        const rts_row_params &p = params[r];
+        const long long rr = (long long)r;
+        if (std::isnan(p.temperature) || std::isinf(p.temperature))
+            return fail(RTS_EINVAL, "row %lld: temperature is not finite", rr);
+        const bool greedy = !(p.temperature > 0.0f);
+        if (!greedy && (p.top_k < 1 || p.top_k > RTS_MAX_TOP_K))
+            return fail(RTS_EINVAL, "row %lld: top_k = %d outside 1..64 on a sampled row", rr, p.top_k);
+        if (!(p.top_p > 0.0f && p.top_p <= 1.0f))
+            return fail(RTS_EINVAL, "row %lld: top_p = %g outside (0, 1]", rr, (double)p.top_p);
+        if (!(p.min_p >= 0.0f && p.min_p <= 1.0f))
+            return fail(RTS_EINVAL, "row %lld: min_p = %g outside [0, 1]", rr, (double)p.min_p);
+        if (!(p.penalty_repeat > 0.0f) || std::isinf(p.penalty_repeat))
+            return fail(RTS_EINVAL, "row %lld: penalty_repeat = %g must be finite > 0", rr,
+                        (double)p.penalty_repeat);
+        if (!std::isfinite(p.penalty_freq) || !std::isfinite(p.penalty_present))
+            return fail(RTS_EINVAL, "row %lld: penalty_freq / penalty_present not finite", rr);
+        if (p.penalty_last_n < -1)
+            return fail(RTS_EINVAL, "row %lld: penalty_last_n = %d < -1", rr, p.penalty_last_n);
+        if (p.history_row < -1)
+            return fail(RTS_EINVAL, "row %lld: history_row = %d < -1", rr, p.history_row);
+        if (p.reserved != 0) return fail(RTS_EINVAL, "row %lld: reserved field is not 0", rr);
+        if (p.history_row >= 0) {
+            if (history == nullptr || history_len == nullptr)
+                return fail(RTS_EINVAL, "row %lld: history_row set without history", rr);
+            if (p.history_row >= H)
+                return fail(RTS_EINVAL, "row %lld: history_row = %d >= H = %lld", rr,
+                            p.history_row, (long long)H);
+            const int32_t hl = history_len[p.history_row];
+            if (hl < 0 || hl > ldh)
+                return fail(RTS_EINVAL, "history row %d: length %d outside [0, ldh = %lld]",
+                            p.history_row, hl, (long long)ldh);
+            const int64_t n_eff = p.penalty_last_n < 0 ? hl
+                                  : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
+            if (n_eff > RTS_MAX_WINDOW)
+                return fail(RTS_EINVAL, "row %lld: penalty window of %lld ids > %d", rr,
+                            (long long)n_eff, RTS_MAX_WINDOW);
+        }
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
+        const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
+        const int ept = choose_ept(rows, V);
+        rts::SampleArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.logits = logits + r0 * ld;
+        a.ld = ld;
+        a.history = history;
+        a.keys = reinterpret_cast<uint64_t *>(ws + rts::kTicketBytes);
+        a.tickets = reinterpret_cast<uint32_t *>(ws);
+        a.token = token + r0;
+        a.counts = counts ? counts + 3 * r0 : nullptr;
+        a.kept_ids = kept_ids ? kept_ids + rts::kMaxK * r0 : nullptr;
+        a.kept_logits = kept_logits ? kept_logits + rts::kMaxK * r0 : nullptr;
+        a.philox_x0 = philox_x0 ? philox_x0 + r0 : nullptr;
+        a.V = (int32_t)V;
+        a.nchunks = (int32_t)chunks_for(V, ept);
+        a.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
+        a.rows = rows;
+        for (int i = 0; i < rows; ++i) {
+            const rts_row_params &p = params[r0 + i];
+            rts::SampleRow &s = a.row[i];
+            const bool greedy = !(p.temperature > 0.0f);
+            const int64_t k_eff = greedy ? 1 : (p.top_k < V ? p.top_k : V);
+            int64_t n_eff = 0, hist_off = 0;
+            const bool neutral = p.penalty_repeat == 1.0f && p.penalty_freq == 0.0f &&
+                                 p.penalty_present == 0.0f;
+            if (p.history_row >= 0 && !neutral) {
+                const int32_t hl = history_len[p.history_row];
+                n_eff = p.penalty_last_n < 0 ? hl : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
+                hist_off = (int64_t)p.history_row * ldh + (hl - n_eff);
+            }
+            s.seed = p.seed;
+            s.counter = p.counter;
+            s.hist_off = hist_off;
+            s.lnp = logf(p.min_p);
+            s.top_p = p.top_p;
+            s.temperature = p.temperature;
+            s.rep = p.penalty_repeat;
+            s.freq = p.penalty_freq;
+            s.present = p.penalty_present;
+            s.pack = (uint32_t)n_eff | ((uint32_t)k_eff << 16) | (greedy ? (1u << 24) : 0u);
+        }
+        const int e = rts::launch_sample(a, ept, is_vec_ok(a.logits, ld), stream);
+        if (e != 0)
+            return fail(RTS_EDEVICE, "sample launch (rows %lld..%lld): %s", (long long)r0,
+                        (long long)(r0 + rows - 1), hipGetErrorString((hipError_t)e));
+    }
+    return RTS_OK;
+}
+
+int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
+                       const int32_t *tokens, int32_t top_n,
+                       const int32_t *allowed, const int64_t *allowed_off,
+                       float *token_lp, int32_t *top_ids, float *top_lp,
+                       void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (B == 0) return RTS_OK;
+    if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
+    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
+    if (logits == nullptr || tokens == nullptr || token_lp == nullptr)
+        return fail(RTS_EINVAL, "logits, tokens and token_lp must not be NULL");
+    if (top_n < 0 || top_n > RTS_MAX_TOP_N)
+        return fail(RTS_EINVAL, "top_n = %d outside 0..20", top_n);
+    if (top_n > 0 && (top_ids == nullptr || top_lp == nullptr))
+        return fail(RTS_EINVAL, "top_ids / top_lp are NULL with top_n = %d", top_n);
+    if (allowed != nullptr && allowed_off == nullptr)
+        return fail(RTS_EINVAL, "allowed without allowed_off");
+    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
+    size_t need = 0;
+    rts_workspace_bytes(B, V, &need);
+    if (ws_bytes < need)
+        return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+
+    const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
+    bool any_restricted = false;
+    if (allowed != nullptr) {
+        if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");
+        for (int64_t r = 0; r < B; ++r) {
+            if (allowed_off[r + 1] < allowed_off[r])
+                return fail(RTS_EINVAL, "allowed_off decreases at row %lld", (long long)r);
+            if (allowed_off[r + 1] > allowed_off[r]) any_restricted = true;
+        }
+        if (any_restricted) {
+            const size_t lds = bitmap_bytes + rts::kAllowedStaticLds;
+            if (V > (1 << 19) || lds > max_lds_per_block())
+                return fail(RTS_EINVAL, "allowed lists need V <= 2^19 (V = %lld)", (long long)V);
+        }
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    rts::LogprobArgs base;
+    std::memset(&base, 0, sizeof base);
+    base.logits = logits;
+    base.ld = ld;
+    base.tokens = tokens;
+    base.allowed = allowed;
+    base.keys = reinterpret_cast<uint64_t *>(ws + rts::kTicketBytes);
+    base.tickets = reinterpret_cast<uint32_t *>(ws + 256);
+    base.token_lp = token_lp;
+    base.top_ids = top_ids;
+    base.top_lp = top_lp;
+    base.V = (int32_t)V;
+    base.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
+    base.partial_stride = (int32_t)rts::max_chunks(V);
+    base.top_n = top_n;
+    const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
+    base.partials = reinterpret_cast<float2 *>(ws + rts::kTicketBytes +
+                                               (size_t)rows_ws * rts::keys_bytes_per_row(V));
+
+    // Unrestricted rows through the full-row reducer, restricted rows through
+    // the gather kernel; each in launches of up to 64 rows.
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool want_restricted = pass == 1;
+        if (want_restricted && !any_restricted) break;
+        rts::LogprobArgs a = base;
+        int n = 0;
+        auto flush = [&]() -> int {
+            if (n == 0) return 0;
+            a.rows = n;
+            int e;
+            if (want_restricted) {
+                e = rts::launch_logprobs_allowed(a, bitmap_bytes, stream);
+            } else {
+                const int ept = choose_ept(n, V);
+                a.nchunks = (int32_t)chunks_for(V, ept);
+                const bool vec = is_vec_ok(logits, ld);
+                e = rts::launch_logprobs_full(a, ept, vec, stream);
+            }
+            n = 0;
+            return e;
+        };
+        for (int64_t r = 0; r < B; ++r) {
+            const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
+            if ((cnt > 0) != want_restricted) continue;
+            rts::LogprobRow &lr = a.row[n++];
+            lr.row = (int32_t)r;
+            lr.allowed_off = allowed ? allowed_off[r] : 0;
+            lr.allowed_cnt = cnt;
+            lr.pad = 0;
+            if (n == rts::kRowsPerLaunch) {
+                const int e = flush();
+                if (e != 0)
+                    return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
+            }
+        }
+        const int e = flush();
+        if (e != 0) return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    return RTS_OK;
+}
+
+}  // extern "C"

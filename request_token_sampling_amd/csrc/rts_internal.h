@@ -1,0 +1,96 @@
+// rts_internal.h -- launch descriptors shared by the C-ABI host code and the
+// kernels.  Per-row parameters travel in the kernel-argument block, so a call
+// needs no host-to-device copy and no staging buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rts {
+
+constexpr int kBlock = 256;          // threads per workgroup: four 64-lane waves
+constexpr int kRowsPerLaunch = 64;   // rows whose parameters fit one argument block
+constexpr int kMinChunk = 1024;      // smallest chunk of a row handled by one workgroup
+constexpr int kMaxK = 64;            // largest top_k
+constexpr int kMaxTopN = 20;         // largest top_logprobs
+
+// Workspace layout (bytes from its start):
+//   [0, 256)     sampling tickets, one uint32 per row slot of a launch
+//   [256, 512)   logprob tickets
+//   [512, ...)   per row slot: chunk candidate keys, then logprob partials
+constexpr size_t kTicketBytes = 512;
+
+// Static LDS of the allowed-ids kernel besides its vocabulary bitmap.
+constexpr size_t kAllowedStaticLds = 6144;
+
+inline int64_t max_chunks(int64_t V) { return (V + kMinChunk - 1) / kMinChunk; }
+inline size_t keys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxK * 8u; }
+inline size_t partial_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * 8u; }
+
+// Per-row sampling parameters after host-side checking (56 bytes).
+struct SampleRow {
+    uint64_t seed;
+    uint64_t counter;
+    int64_t hist_off;      // element offset of the window's first id in `history`
+    float lnp;             // logf(min_p); -inf for min_p = 0
+    float top_p;
+    float temperature;
+    float rep;
+    float freq;
+    float present;
+    uint32_t pack;         // bits 0..15 window length, 16..22 k_eff, 24 greedy
+};
+static_assert(sizeof(SampleRow) == 56, "argument block layout");
+
+struct SampleArgs {
+    const float *logits;   // row 0 of this launch
+    int64_t ld;
+    const int32_t *history;
+    uint64_t *keys;        // workspace: per row slot nchunks * k_eff keys
+    uint32_t *tickets;
+    int32_t *token;        // outputs, row 0 of this launch
+    int32_t *counts;
+    int32_t *kept_ids;
+    float *kept_logits;
+    uint32_t *philox_x0;
+    int32_t V;
+    int32_t nchunks;
+    int32_t keys_stride;   // keys per row slot in the workspace
+    int32_t rows;
+    SampleRow row[kRowsPerLaunch];
+};
+
+struct LogprobRow {
+    int64_t allowed_off;   // first id of the row's list in `allowed`
+    int64_t allowed_cnt;   // 0: unrestricted
+    int32_t row;           // row index within the launch's logits / outputs
+    int32_t pad;
+};
+
+struct LogprobArgs {
+    const float *logits;
+    int64_t ld;
+    const int32_t *tokens;
+    const int32_t *allowed;
+    uint64_t *keys;
+    float2 *partials;
+    uint32_t *tickets;
+    float *token_lp;
+    int32_t *top_ids;
+    float *top_lp;
+    int32_t V;
+    int32_t nchunks;
+    int32_t keys_stride;
+    int32_t partial_stride;
+    int32_t top_n;
+    int32_t rows;
+    LogprobRow row[kRowsPerLaunch];
+};
+
+// Launchers (return a hipError_t as int).
+int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
+int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s);
+int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, hipStream_t s);
+int launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
+
+}  // namespace rts

@@ -1,0 +1,106 @@
+"""Helpers for GPU-vs-oracle parity.  Expected values come only from the
+CPU oracle; the HIP path's outputs are only ever compared against them.
+
+Bar (bit-exact unless stated):
+  kept ids and their order, kept logits, k_eff, the min_p count m, the
+  Philox word x0; the top_p count n and the sampled id, except on rows the
+  oracle flags as within 1e-6 of a top_p or CDF boundary, where two correct
+  fp64 evaluations (different exp implementations, summation order) may
+  differ -- there the GPU's token must still be one of the kept ids;
+  logprobs within 1e-5 absolute, top logprob ids exact.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle.oracle as O
+import request_token_sampling_amd as R
+from request_token_sampling_amd import workloads as W
+
+LP_ATOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def gpu_sample(logits, params, history=None, hist_len=None, logits_dev=None):
+    x = logits_dev if logits_dev is not None else to_dev(np.asarray(logits, np.float32))
+    h = None if history is None else to_dev(np.asarray(history, np.int32))
+    out = R.sample_tokens(x, params, h, hist_len)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def oracle_sample(logits, params, history=None, hist_len=None):
+    return O.sample_tokens(np.asarray(logits, np.float32), params, history, hist_len)
+
+
+def compare_sample(g, o, tag=""):
+    """Assert the bar above row by row; returns the number of flagged rows."""
+    B = o["token"].shape[0]
+    flagged = 0
+    x0g = g["philox_x0"].view(np.uint32)
+    for r in range(B):
+        k = int(o["counts"][r, 0])
+        where = f"{tag} row {r}"
+        assert int(g["counts"][r, 0]) == k, (where, "k_eff", g["counts"][r], o["counts"][r])
+        assert np.array_equal(g["kept_ids"][r], o["kept_ids"][r]), (
+            where, "kept_ids", g["kept_ids"][r][:k], o["kept_ids"][r][:k])
+        assert np.array_equal(g["kept_logits"][r], o["kept_logits"][r]), (
+            where, "kept_logits", g["kept_logits"][r][:k], o["kept_logits"][r][:k])
+        assert int(g["counts"][r, 1]) == int(o["counts"][r, 1]), (where, "m", g["counts"][r],
+                                                                  o["counts"][r])
+        assert int(x0g[r]) == int(o["x0"][r]), (where, "x0")
+        fl = int(o["flags"][r])
+        flagged += 1 if fl else 0
+        if not fl & O.FLAG_TOP_P_EDGE:
+            assert int(g["counts"][r, 2]) == int(o["counts"][r, 2]), (where, "n", g["counts"][r],
+                                                                      o["counts"][r])
+        if fl:
+            n = max(int(g["counts"][r, 2]), int(o["counts"][r, 2]))
+            assert int(g["token"][r]) in set(o["kept_ids"][r][:n].tolist()), (where, "token")
+        else:
+            assert int(g["token"][r]) == int(o["token"][r]), (where, "token", g["token"][r],
+                                                              o["token"][r], o["u"][r])
+    return flagged
+
+
+def gpu_logprobs(logits, tokens, top_n, allowed_lists=None, logits_dev=None):
+    x = logits_dev if logits_dev is not None else to_dev(np.asarray(logits, np.float32))
+    t = to_dev(np.asarray(tokens, np.int32))
+    if allowed_lists is not None:
+        ids, off = W.pack_allowed(allowed_lists)
+        out = R.token_logprobs(x, t, top_n, to_dev(ids) if ids.size else
+                               torch.zeros(1, dtype=torch.int32, device="cuda"), off)
+    else:
+        out = R.token_logprobs(x, t, top_n)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def compare_logprobs(g, o, tag=""):
+    B = o["token_lp"].shape[0]
+    for r in range(B):
+        where = f"{tag} row {r}"
+        a, b = float(g["token_lp"][r]), float(o["token_lp"][r])
+        if np.isinf(b):
+            assert a == b, (where, "token_lp", a, b)
+        else:
+            assert abs(a - b) <= LP_ATOL, (where, "token_lp", a, b)
+        assert np.array_equal(g["top_ids"][r], o["top_ids"][r]), (where, "top_ids",
+                                                                  g["top_ids"][r], o["top_ids"][r])
+        gl, ol = g["top_lp"][r].astype(np.float64), o["top_lp"][r]
+        fin = np.isfinite(ol)
+        assert np.array_equal(np.isfinite(gl), fin), (where, "top_lp pad")
+        assert np.all(np.abs(gl[fin] - ol[fin]) <= LP_ATOL), (where, "top_lp",
+                                                             np.max(np.abs(gl[fin] - ol[fin])))

@@ -1,0 +1,174 @@
+"""C-ABI boundary on the CPU: the library loads, exports every function that
+include/*.h declares, and refuses bad arguments before touching the GPU.
+
+Pointers passed here are fake non-NULL addresses: every call below fails in
+host validation, which runs before anything is enqueued, so no HIP call is
+made and nothing is dereferenced."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import request_token_sampling_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(4096)
+BIG_WS = 1 << 40
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(rts_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"rts_sample_tokens", "rts_token_logprobs", "rts_workspace_bytes",
+            "rts_workspace_init", "rts_strerror", "rts_last_error"} <= names
+    L = R.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layout_matches_header():
+    text = open(os.path.join(ROOT, "include", "rts.h")).read()
+    body = text[text.index("typedef struct rts_row_params"):text.index("} rts_row_params;")]
+    fields = re.findall(r"^\s*(?:float|int32_t|uint64_t)\s+(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in R.RowParams._fields_]
+    assert ctypes.sizeof(R.RowParams) == 56
+
+
+def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws_bytes=BIG_WS,
+           history=None, H=0, ldh=0, hist_len=None):
+    L = R.lib()
+    arr = R.row_params(params)
+    B = len(params) if B is None else B
+    hl = None
+    if hist_len is not None:
+        hl = (ctypes.c_int32 * len(hist_len))(*hist_len)
+    return L.rts_sample_tokens(logits, B, V, V if ld is None else ld, arr, history, H, ldh, hl,
+                               token, None, None, None, None, ws, ws_bytes, None)
+
+
+SAMPLED = dict(temperature=0.7, top_k=20, top_p=0.9, min_p=0.05, seed=1, counter=0)
+
+
+def last_error():
+    return R.lib().rts_last_error().decode()
+
+
+@pytest.mark.parametrize("bad,field", [
+    (dict(top_k=0), "top_k"),
+    (dict(top_k=65), "top_k"),
+    (dict(top_k=-3), "top_k"),
+    (dict(temperature=float("nan")), "temperature"),
+    (dict(temperature=float("inf")), "temperature"),
+    (dict(top_p=0.0), "top_p"),
+    (dict(top_p=1.5), "top_p"),
+    (dict(top_p=float("nan")), "top_p"),
+    (dict(min_p=-0.1), "min_p"),
+    (dict(min_p=1.01), "min_p"),
+    (dict(penalty_repeat=0.0), "penalty_repeat"),
+    (dict(penalty_repeat=-1.0), "penalty_repeat"),
+    (dict(penalty_repeat=float("inf")), "penalty_repeat"),
+    (dict(penalty_freq=float("nan")), "penalty_freq"),
+    (dict(penalty_present=float("inf")), "penalty_present"),
+    (dict(penalty_last_n=-2), "penalty_last_n"),
+    (dict(history_row=-2), "history_row"),
+    (dict(history_row=0), "history"),
+    (dict(reserved=1), "reserved"),
+])
+def test_bad_row_is_refused_and_named(bad, field):
+    rows = [dict(SAMPLED) for _ in range(5)]
+    rows[3].update(bad)
+    assert sample(rows) == R.RTS_EINVAL
+    msg = last_error()
+    assert "row 3" in msg and field in msg, msg
+
+
+def test_greedy_rows_ignore_top_k():
+    # a greedy row with top_k = 0 is valid: the failure comes from a later row
+    rows = [dict(temperature=0.0, top_k=0), dict(SAMPLED, top_k=0)]
+    assert sample(rows) == R.RTS_EINVAL
+    assert "row 1" in last_error()
+
+
+def test_bad_shapes_and_pointers():
+    rows = [dict(SAMPLED)]
+    assert sample(rows, B=-1) == R.RTS_EINVAL
+    assert sample(rows, V=0) == R.RTS_EINVAL
+    assert sample(rows, V=2**31) == R.RTS_EINVAL
+    assert sample(rows, ld=999) == R.RTS_EINVAL and "ld" in last_error()
+    assert sample(rows, logits=None) == R.RTS_EINVAL and "logits" in last_error()
+    assert sample(rows, token=None) == R.RTS_EINVAL and "token" in last_error()
+    assert sample(rows, ws=None) == R.RTS_EINVAL
+
+
+def test_short_workspace():
+    need = R.workspace_bytes(1, 1000)
+    assert sample([dict(SAMPLED)], ws_bytes=need - 1) == R.RTS_ENOSPC
+    assert "workspace" in last_error()
+
+
+def test_empty_batch_is_a_noop():
+    assert sample([dict(SAMPLED)], B=0) == R.RTS_OK
+    assert last_error() == ""
+
+
+def test_history_checks():
+    hist = FAKE
+    rows = [dict(SAMPLED, history_row=1, penalty_last_n=64, penalty_repeat=1.1)]
+    assert sample(rows, history=hist, H=1, ldh=64, hist_len=[64]) == R.RTS_EINVAL
+    assert "history_row" in last_error()
+    rows = [dict(SAMPLED, history_row=0, penalty_last_n=-1, penalty_repeat=1.1)]
+    assert sample(rows, history=hist, H=1, ldh=64, hist_len=[65]) == R.RTS_EINVAL
+    assert "length" in last_error()
+    assert sample(rows, history=hist, H=1, ldh=70000, hist_len=[66000]) == R.RTS_EINVAL
+    assert "window" in last_error()
+
+
+def test_workspace_bytes():
+    a = R.workspace_bytes(1, 248_320)
+    b = R.workspace_bytes(40, 248_320)
+    c = R.workspace_bytes(64, 248_320)
+    d = R.workspace_bytes(1000, 248_320)
+    assert 0 < a < b < c == d        # launches of up to 64 rows reuse one region
+    assert R.workspace_bytes(64, 1024) % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert R.lib().rts_workspace_bytes(-1, 10, ctypes.byref(n)) == R.RTS_EINVAL
+    assert R.lib().rts_workspace_bytes(1, 0, ctypes.byref(n)) == R.RTS_EINVAL
+
+
+def logprobs(B=2, V=1000, ld=None, tokens=FAKE, top_n=5, allowed=None, off=None, lp=FAKE,
+             ids=FAKE, tlp=FAKE, ws_bytes=BIG_WS):
+    offa = None if off is None else (ctypes.c_int64 * len(off))(*off)
+    return R.lib().rts_token_logprobs(FAKE, B, V, V if ld is None else ld, tokens, top_n,
+                                      allowed, offa, lp, ids, tlp, FAKE, ws_bytes, None)
+
+
+def test_logprob_argument_checks():
+    assert logprobs(top_n=21) == R.RTS_EINVAL and "top_n" in last_error()
+    assert logprobs(top_n=-1) == R.RTS_EINVAL
+    assert logprobs(ids=None) == R.RTS_EINVAL
+    assert logprobs(tokens=None) == R.RTS_EINVAL
+    assert logprobs(lp=None) == R.RTS_EINVAL
+    assert logprobs(ld=10) == R.RTS_EINVAL
+    assert logprobs(allowed=FAKE, off=None) == R.RTS_EINVAL
+    assert logprobs(allowed=FAKE, off=[0, 5, 3]) == R.RTS_EINVAL and "decreases" in last_error()
+    assert logprobs(allowed=FAKE, off=[-1, 5, 6]) == R.RTS_EINVAL
+    assert logprobs(V=(1 << 19) + 1, allowed=FAKE, off=[0, 5, 6]) == R.RTS_EINVAL
+    assert logprobs(ws_bytes=100) == R.RTS_ENOSPC
+    assert logprobs(B=0) == R.RTS_OK
+
+
+def test_strerror():
+    L = R.lib()
+    for code in (0, -1, -2, -3, 7):
+        assert L.rts_strerror(code)
