@@ -1,0 +1,269 @@
+"""Benchmark of the per-token sampler on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single_stream|window|batch|stress]
+
+A step is one pass of the hot path over one batch of the workload:
+  single_stream  one row of 248,320 fp32 logits, the sampled chain (top_k 20,
+                 top_p 0.8, temperature 0.7) and a greedy pass over the row;
+  window         a verify window of 5 rows with penalties over a 64-id history;
+  batch          40 rows (8 slots x 5) with per-row parameters and penalties;
+  stress         40 bf16-grid rows sampled at top_k 64, then top-20 logprobs,
+                 unrestricted and over 1,000 allowed ids per row.
+Logits are resident in HBM before timing.  Each step reads a different copy of
+the batch, rotating through at least 512 MiB of copies, so the reads come
+from HBM and not from the 256 MiB MALL.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sampled rows/sec + achieved HBM GB/s (% peak) at V=248,320, top_k=20"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 512 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="single_stream",
+                    choices=["single_stream", "window", "batch", "stress"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads' figures in the JSON line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+class Workload:
+    """Device-resident copies of one batch plus the calls of one step."""
+
+    def __init__(self, name, dev):
+        import numpy as np
+        import torch
+
+        import request_token_sampling_amd as R
+        from request_token_sampling_amd import workloads as W
+
+        self.name = name
+        self.passes = []          # list of (label, params array, rows_counted_as_sampled)
+        self.logprob = None
+        hist = hist_len = None
+        if name == "single_stream":
+            w = W.single_stream()
+            x = w["logits"]
+            self.passes = [("sampled", R.row_params(w["sampled"]), 1),
+                           ("greedy", R.row_params(w["greedy"]), 0)]
+            self.desc = ("single stream: 1 row, V=248,320 fp32 N(0,3) with 3 spiked heads; "
+                         "top_k 20, top_p 0.8, min_p 0, temperature 0.7, no penalties; "
+                         "plus a greedy pass over the same row")
+        elif name == "window":
+            vw = W.VerifyWindows()
+            x = vw.next_logits()
+            hist = vw.history.reshape(1, -1)
+            hist_len = [hist.shape[1]]
+            self.passes = [("sampled", R.row_params(vw.params(0)), 5)]
+            self.desc = ("verify window: 5 rows, V=248,320, penalties 1.1/0.5/0.5 over a "
+                         "64-id history, top_k 40, min_p 0.05, top_p 0.95, temperature 1")
+        elif name == "batch":
+            w = W.batch_slots()
+            x, hist, hist_len = w["logits"], w["history"], w["hist_len"]
+            self.passes = [("sampled", R.row_params(w["params"]), 40)]
+            self.desc = ("batch slots: 40 rows, V=248,320, per-row T/top_k/top_p/min_p, "
+                         "penalties over 256 Zipf history ids per slot")
+        else:
+            w = W.logprobs_stress()
+            x = w["logits"]
+            self.passes = [("sampled", R.row_params(w["params"]), 40)]
+            ids, off = W.pack_allowed(w["allowed"])
+            self.logprob = (w["top_n"], torch.from_numpy(ids).to(dev), off)
+            self.desc = ("logprobs stress: 40 bf16-grid rows, V=248,320, top_k 64, min_p 0.1; "
+                         "top-20 logprobs unrestricted and over 1,000 allowed ids per row")
+        self.B, self.V = x.shape
+        self.row_bytes = self.V * 4
+        batch_bytes = self.B * self.row_bytes
+        self.ncopies = max(2, math.ceil(ROTATE_BYTES / batch_bytes))
+        base = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        self.copies = base.unsqueeze(0).repeat(self.ncopies, 1, 1)
+        self.hist = None if hist is None else torch.from_numpy(np.asarray(hist, np.int32)).to(dev)
+        self.hist_len = hist_len
+        self.ws = R.make_workspace(self.B, self.V, dev)
+        stream = torch.cuda.current_stream()
+        self.calls = [R.SampleCall(self.copies[0], p, self.hist, hist_len, workspace=self.ws,
+                                   stream=stream) for _, p, _ in self.passes]
+        self.sampled_rows = sum(n for _, _, n in self.passes)
+        self.tokens = self.calls[0].token
+        self.R = R
+        self.torch = torch
+
+    def step(self, i, events=None):
+        x = self.copies[i % self.ncopies]
+        for j, c in enumerate(self.calls):
+            c.logits = x
+            if events is not None:
+                events[j][0].record()
+            c()
+            if events is not None:
+                events[j][1].record()
+        if self.logprob is not None:
+            top_n, ids, off = self.logprob
+            self.R.token_logprobs(x, self.tokens, top_n, workspace=self.ws)
+            self.R.token_logprobs(x, self.tokens, top_n, ids, off, workspace=self.ws)
+
+
+def time_workload(wl, steps, warmup):
+    """Wall time of `steps` steps, and the average HIP-event duration of each
+    sampler call (events recorded on the stream the kernels run on)."""
+    torch = wl.torch
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] for _ in wl.calls]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(warmup + i, [(e[i][0], e[i][1]) for e in ev])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [sum(a.elapsed_time(b) for a, b in e) / steps for e in ev]
+    return wall, kern_ms
+
+
+def roofline(wl, kern_ms):
+    """HBM roofline of the sampled-chain kernel: algorithmic bytes per launch
+    (one read of every logit row, plus outputs) over its average duration."""
+    out_bytes = wl.B * (4 + 12 + 256 + 256 + 4)
+    alg = wl.B * wl.row_bytes + out_bytes
+    dur_s = kern_ms[0] * 1e-3
+    achieved = alg / dur_s / 1e9
+    return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=read_traffic(wl.name),
+                kernel="sample_kernel", algorithmic_bytes_per_launch=alg,
+                avg_launch_us=round(kern_ms[0] * 1e3, 3))
+
+
+def read_traffic(workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"traffic_sample_kernel_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "request_token_sampling_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(seconds):
+    """The oracle as it stands, single-threaded, on the single-stream row
+    (sampled pass plus greedy pass, as one GPU step), for about `seconds`."""
+    import oracle.oracle as O
+    from request_token_sampling_amd import workloads as W
+    w = W.single_stream()
+    x = w["logits"]
+    O.sample_tokens(x, w["sampled"])
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        O.sample_tokens(x, w["sampled"])
+        O.sample_tokens(x, w["greedy"])
+        n += 1
+    dt = time.perf_counter() - t0
+    return dict(value=round(n / dt, 3), unit="rows/s", cores=1, kind="oracle",
+                sample=f"{n} single-stream steps (one sampled row of V=248,320 plus its greedy "
+                       f"pass) in {dt:.1f} s on one host thread")
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the sampler's rows are independent and this "
+              "build runs on a single MI355X; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    wl = Workload(args.workload, dev)
+    progress(f"{args.workload}: {wl.ncopies} copies resident, timing {args.steps} steps")
+    wall, kern_ms = time_workload(wl, args.steps, args.warmup)
+    progress(f"{args.workload}: {wall / args.steps * 1e3:.4f} ms/step, kernels {kern_ms}")
+    ms_step = wall / args.steps * 1e3
+    value = wl.sampled_rows * args.steps / wall
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.desc, "rows_per_step": wl.B, "V": wl.V,
+                   "passes_per_step": [p[0] for p in wl.passes] +
+                   (["logprobs", "logprobs_allowed"] if wl.logprob else []),
+                   "logit_copies_rotated": wl.ncopies, "device": props.name},
+        "roofline": roofline(wl, kern_ms),
+        "kernel_us_per_call": [round(m * 1e3, 3) for m in kern_ms],
+    }
+    if not args.no_extra:
+        extra = {}
+        for name in ("batch", "stress", "window"):
+            if name == args.workload:
+                continue
+            w2 = Workload(name, dev)
+            steps = max(50, args.steps // 4)
+            wall2, k2 = time_workload(w2, steps, max(10, args.warmup // 4))
+            progress(f"{name}: {wall2 / steps * 1e3:.4f} ms/step, kernels {k2}")
+            extra[name] = dict(value=round(w2.sampled_rows * steps / wall2, 1), unit="rows/s",
+                               ms_per_step=round(wall2 / steps * 1e3, 5),
+                               roofline=roofline(w2, k2), desc=w2.desc)
+            del w2
+            torch.cuda.empty_cache()
+        line["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        progress(f"oracle on the host for about {args.cpu_seconds} s")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

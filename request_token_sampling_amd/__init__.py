@@ -159,17 +159,23 @@ class SampleCall:
 
     def set_params(self, params):
         self.params = params if isinstance(params, ctypes.Array) else row_params(params)
+        self._args = None
 
-    def __call__(self):
-        L = lib()
-        rc = L.rts_sample_tokens(
-            _ptr(self.logits), self.B, self.V, self.ld, self.params,
+    def _build_args(self):
+        self._args = [
+            None, self.B, self.V, self.ld, self.params,
             _ptr(self.history), self.H, self.ldh,
             None if self.hist_len is None else self.hist_len.ctypes.data_as(ctypes.c_void_p),
             _ptr(self.token), _ptr(self.counts), _ptr(self.kept_ids), _ptr(self.kept_logits),
-            _ptr(self.philox_x0), _ptr(self.workspace), self.workspace.numel(),
-            _stream_handle(self.stream))
-        _check(rc)
+            _ptr(self.philox_x0), _ptr(self.workspace), self.workspace.numel(), None]
+
+    def __call__(self):
+        if self._args is None:
+            self._build_args()
+        a = self._args
+        a[0] = self.logits.data_ptr()
+        a[16] = _stream_handle(self.stream)
+        _check(lib().rts_sample_tokens(*a))
         return self
 
     def results(self) -> dict:

@@ -65,23 +65,6 @@ __device__ __forceinline__ uint64_t lanes_below_mask()
     return (1ull << lane_id()) - 1ull;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m)
-{
-    const int lo = __shfl_xor((int)(uint32_t)v, m, 64);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
 __device__ __forceinline__ float wave_max_f32(float v)
 {
 #pragma unroll
@@ -96,16 +79,86 @@ __device__ __forceinline__ double wave_sum_f64(double v)
     return v;
 }
 
-// Inclusive prefix sum over the 64 lanes (Hillis-Steele).
-__device__ __forceinline__ double wave_scan_f64(double v)
+// ---------------------------------------------------------------------------
+// DPP (data-parallel primitives) cross-lane steps.  Row ops move data inside
+// 16-lane rows; row_bcast15/31 carry a row's last lane into the next rows.
+// Lanes whose source is out of range or masked off read 0, the identity of
+// the sums and unsigned maxima below.  These stay in the VALU, unlike
+// ds_bpermute-based shuffles.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
 {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const double o = __shfl_up(v, (unsigned)d, 64);
-        if (lane >= d) v += o;
-    }
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)b);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x)
+{
+    const uint32_t lo = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)x);
+    const uint32_t hi = dpp_u32<CTRL, ROW_MASK, BANK_MASK>((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr3 = 0x113, kRowShr4 = 0x114,
+              kRowShr8 = 0x118, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the 64 lanes: within rows by shifts of 1..3, 4
+// and 8, then across rows by the two broadcasts.
+__device__ __forceinline__ double wave_scan_f64(double x)
+{
+    double s = x + dpp_f64<kRowShr1>(x);
+    s = s + dpp_f64<kRowShr2>(x);
+    s = s + dpp_f64<kRowShr3>(x);
+    s = s + dpp_f64<kRowShr4, 0xF, 0xE>(s);
+    s = s + dpp_f64<kRowShr8, 0xF, 0xC>(s);
+    s = s + dpp_f64<kRowBcast15, 0xA, 0xF>(s);
+    s = s + dpp_f64<kRowBcast31, 0xC, 0xF>(s);
+    return s;
+}
+
+// Inclusive running maximum of unsigned 64-bit keys; lane 63 holds the
+// maximum of the wave.
+__device__ __forceinline__ uint64_t wave_scan_max_u64(uint64_t v)
+{
+    uint64_t o;
+    o = dpp_u64<kRowShr1>(v); v = o > v ? o : v;
+    o = dpp_u64<kRowShr2>(v); v = o > v ? o : v;
+    o = dpp_u64<kRowShr4, 0xF, 0xE>(v); v = o > v ? o : v;
+    o = dpp_u64<kRowShr8, 0xF, 0xC>(v); v = o > v ? o : v;
+    o = dpp_u64<kRowBcast15, 0xA, 0xF>(v); v = o > v ? o : v;
+    o = dpp_u64<kRowBcast31, 0xC, 0xF>(v); v = o > v ? o : v;
     return v;
+}
+
+// Values of one lane (uniform lane index) in every lane.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ int32_t lane_i32(int32_t v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ float lane_f32(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double lane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t r = ((uint64_t)lane_u32((uint32_t)(b >> 32), l) << 32) | lane_u32((uint32_t)b, l);
+    return __longlong_as_double((long long)r);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
+{
+    return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | lane_u32((uint32_t)v, l);
 }
 
 // Largest t (to `bits` leading bits) with #{keys >= t} >= k, over the four
@@ -150,21 +203,46 @@ __device__ __forceinline__ uint32_t philox4x32_10_x0(uint64_t counter, uint64_t 
     return c0;
 }
 
-// Row-completion ticket: every workgroup of a row publishes its results,
+// ---------------------------------------------------------------------------
+// Row-completion protocol.  Every workgroup of a row publishes its results,
 // then takes a ticket; the one drawing the last ticket merges the row.
-// Release/acquire at agent scope so stores from other XCDs are visible.
+//
+// The published words are written with device-scope (agent) atomic stores and
+// read back with device-scope atomic loads: on gfx950 these carry the device
+// coherence bit, so they are written through to, and read from, the level
+// shared by all XCDs, not an XCD's private L2.  Each thread waits for its
+// stores to complete (vmcnt = 0) before the workgroup barrier, and only then
+// does one thread take the ticket with a device-scope atomic add.  A release
+// fence at agent scope would also order them, but it writes back the whole
+// L2 of the XCD and its acquire invalidates it, once per workgroup; with
+// ~1,000 workgroups per launch that maintenance dominated the kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish_u64(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t read_published_u64(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// s_waitcnt with vmcnt = 0 and the other counters left free (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ bool take_last_ticket(uint32_t *ticket, uint32_t n, uint32_t *s_flag)
 {
-    __threadfence();
+    wait_stores_complete();
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(ticket, 1u);
+        const uint32_t old =
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = (old == n - 1u) ? 1u : 0u;
     }
     __syncthreads();
-    const bool last = *s_flag != 0u;
-    if (last) __threadfence();
-    return last;
+    return *s_flag != 0u;
 }
 
 }  // namespace rts

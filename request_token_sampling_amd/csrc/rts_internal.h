@@ -21,7 +21,7 @@ constexpr int kMaxTopN = 20;         // largest top_logprobs
 constexpr size_t kTicketBytes = 512;
 
 // Static LDS of the allowed-ids kernel besides its vocabulary bitmap.
-constexpr size_t kAllowedStaticLds = 6144;
+constexpr size_t kAllowedStaticLds = 10240;
 
 inline int64_t max_chunks(int64_t V) { return (V + kMinChunk - 1) / kMinChunk; }
 inline size_t keys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxK * 8u; }

@@ -98,7 +98,10 @@ __global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
         for (int e = 0; e < EPT; ++e) lsum += (v[e] == v[e]) ? __expf(v[e] - lmax) : 0.0f;
     }
     const float2 ms = block_max_sum(sm, lmax, lsum);
-    if (tid == 0) a.partials[(int64_t)slot * a.partial_stride + chunk] = ms;
+    if (tid == 0)
+        publish_u64(reinterpret_cast<uint64_t *>(a.partials) + (int64_t)slot * a.partial_stride +
+                        chunk,
+                    ((uint64_t)__float_as_uint(ms.y) << 32) | __float_as_uint(ms.x));
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
     if (K > 0) chunk_topk<EPT>(sm, v, base, K, list + (int64_t)chunk * K);
@@ -112,15 +115,18 @@ __global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
     const int lane = lane_id();
     // fp64 combination of the chunk pairs, each lane taking chunks
     // lane, lane + 64, ... in order, then a fixed-shape wave reduction.
-    const float2 *P = a.partials + (int64_t)slot * a.partial_stride;
+    const uint64_t *P = reinterpret_cast<const uint64_t *>(a.partials) +
+                        (int64_t)slot * a.partial_stride;
     double M = -INFINITY;
-    for (int c = lane; c < a.nchunks; c += 64) M = fmax(M, (double)P[c].x);
+    for (int c = lane; c < a.nchunks; c += 64)
+        M = fmax(M, (double)__uint_as_float((uint32_t)read_published_u64(P + c)));
     for (int d = 32; d >= 1; d >>= 1) M = fmax(M, __shfl_xor(M, d, 64));
     double S = 0.0;
     for (int c = lane; c < a.nchunks; c += 64) {
-        const float2 p = P[c];
-        if (M == -INFINITY) S += (double)p.y;
-        else if (p.x != -INFINITY) S += (double)p.y * exp((double)p.x - M);
+        const uint64_t w = read_published_u64(P + c);
+        const float px = __uint_as_float((uint32_t)w), py = __uint_as_float((uint32_t)(w >> 32));
+        if (M == -INFINITY) S += (double)py;
+        else if (px != -INFINITY) S += (double)py * exp((double)px - M);
     }
     S = wave_sum_f64(S);
     const bool uniform = (M == -INFINITY);

@@ -130,10 +130,18 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
     if (a.kept_ids) a.kept_ids[(int64_t)slot * kMaxK + lane] = id;
     if (a.kept_logits) a.kept_logits[(int64_t)slot * kMaxK + lane] = y;
 
-    const float y0 = __shfl(y, 0, 64);
+    const float y0 = lane_f32(y, 0);
     int m = 1, n = 1, pick = 0;
     uint32_t x0 = 0u;
     if (!greedy) {
+        // Everything that does not depend on the cuts first, so the fp64
+        // exponentials and the Philox rounds overlap: top_p weights
+        // exp(y - y0), tempered weights exp((y - y0) / T), and x0.
+        const double dy = (double)y - (double)y0;
+        const bool head_masked = (y0 == -INFINITY);
+        const double d = (lane < k && !head_masked) ? exp(dy) : 0.0;
+        const double w = (lane < k && !head_masked) ? exp(dy / (double)R.temperature) : 0.0;
+        x0 = philox4x32_10_x0(R.counter, R.seed);
         // min_p: keep the prefix with logit >= head + logf(min_p), in fp32.
         const float thr = y0 + R.lnp;
         m = __popcll(__ballot(lane < k && y >= thr));
@@ -141,29 +149,25 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
         // top_p: shortest prefix of the min_p survivors whose fp64 softmax
         // mass reaches top_p; a masked head (-inf) keeps one candidate.
         n = m;
-        if (y0 == -INFINITY) {
+        if (head_masked) {
             n = 1;
         } else if (!(R.top_p >= 1.0f)) {
-            const double d = (lane < m) ? exp((double)y - (double)y0) : 0.0;
-            const double S = wave_scan_f64(d);
-            const double Z = __shfl(S, m - 1, 64);
+            const double S = wave_scan_f64(lane < m ? d : 0.0);
+            const double Z = lane_f64(S, m - 1);
             const uint64_t b = __ballot(lane < m && S / Z >= (double)R.top_p);
             n = b ? __ffsll((unsigned long long)b) : m;
         }
         // temperature, then the draw: u = x0 / 2^32 against the tempered CDF.
-        x0 = philox4x32_10_x0(R.counter, R.seed);
         const double u = (double)x0 * (1.0 / 4294967296.0);
         pick = n - 1;
         if (n > 1) {
-            const double T = (double)R.temperature;
-            const double w = (lane < n) ? exp(((double)y - (double)y0) / T) : 0.0;
-            const double S = wave_scan_f64(w);
-            const double Z = __shfl(S, n - 1, 64);
+            const double S = wave_scan_f64(lane < n ? w : 0.0);
+            const double Z = lane_f64(S, n - 1);
             const uint64_t b = __ballot(lane < n - 1 && S / Z > u);
             if (b) pick = __ffsll((unsigned long long)b) - 1;
         }
     }
-    const int32_t tok = __shfl(id, pick, 64);
+    const int32_t tok = lane_i32(id, pick);
     if (lane == 0) {
         a.token[slot] = tok;
         if (a.counts) {
