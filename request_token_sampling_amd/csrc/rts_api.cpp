@@ -30,17 +30,19 @@ int fail(int code, const char *fmt, ...)
 void clear_error() { g_last_error[0] = '\0'; }
 
 // Rows per launch and elements per thread.  A launch covers up to 64 rows;
-// each workgroup covers a chunk of 256 * ept elements.  The chunk is the
-// largest whose grid still has >= 512 workgroups (two per CU), so a batch of
-// long rows streams in big chunks and a single row still spreads over the
-// chip; the smallest chunk is 1024 elements.
+// each workgroup covers a chunk of 256 * ept elements.  The per-workgroup
+// selection cost is nearly independent of the chunk size while the row merge
+// grows with the number of chunks, so the chunk is the largest whose grid
+// still has >= 60 workgroups (measured on MI355X at V = 248,320: one row is
+// fastest at 4,096 elements per chunk, 5 and 40 rows at 8,192); the smallest
+// chunk is 1,024 elements.
 int choose_ept(int64_t rows, int64_t V)
 {
     static const int opts[4] = {32, 16, 8, 4};
     for (int i = 0; i < 4; ++i) {
         const int64_t ch = (int64_t)rts::kBlock * opts[i];
         const int64_t nch = (V + ch - 1) / ch;
-        if (rows * nch >= 512) return opts[i];
+        if (rows * nch >= 60) return opts[i];
     }
     return 4;
 }

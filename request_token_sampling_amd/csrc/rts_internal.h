@@ -13,6 +13,9 @@ constexpr int kRowsPerLaunch = 64;   // rows whose parameters fit one argument b
 constexpr int kMinChunk = 1024;      // smallest chunk of a row handled by one workgroup
 constexpr int kMaxK = 64;            // largest top_k
 constexpr int kMaxTopN = 20;         // largest top_logprobs
+// Five waves per SIMD (VGPRs <= 96) keep five 256-thread workgroups resident
+// per CU, 1,280 on the chip: a 40-row batch of 31 chunks fits in one round.
+constexpr int kMinWavesPerSimd = 5;
 
 // Workspace layout (bytes from its start):
 //   [0, 256)     sampling tickets, one uint32 per row slot of a launch

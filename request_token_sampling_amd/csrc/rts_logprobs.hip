@@ -46,7 +46,7 @@ __device__ __forceinline__ float2 block_max_sum(SelectSmem &sm, float m, float s
 }
 
 template <int EPT, bool VEC>
-__global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
+__global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const LogprobArgs a)
 {
     constexpr int CH = EPT * kBlock;
     constexpr int NQ = EPT / 4;
@@ -58,13 +58,13 @@ __global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
     const int row = a.row[slot].row;
     const int V = a.V;
     const int K = a.top_n;
-    const int64_t base = (int64_t)chunk * CH;
+    const int base = chunk * CH;
     const float *x = a.logits + (int64_t)row * a.ld;
 
     float v[EPT];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int64_t i0 = base + q * 1024 + tid * 4;
+        const int i0 = base + q * 1024 + tid * 4;
         if (VEC && i0 + 4 <= V) {
             const f32x4 t = *reinterpret_cast<const f32x4 *>(x + i0);
             v[4 * q + 0] = t.x;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
     int nvalid = 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int64_t i0 = base + q * 1024 + tid * 4;
+        const int i0 = base + q * 1024 + tid * 4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const bool in = i0 + s < V;
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(kBlock) void logprob_kernel(const LogprobArgs a)
                     ((uint64_t)__float_as_uint(ms.y) << 32) | __float_as_uint(ms.x));
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    if (K > 0) chunk_topk<EPT>(sm, v, base, K, list + (int64_t)chunk * K);
+    if (K > 0) chunk_topk<EPT>(sm, v, base, V, K, list + (int64_t)chunk * K);
 
     if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.flag)) return;
 
     // ---- the last workgroup of the row.
-    if (K > 0) list_topk(sm, list, a.nchunks * K, K);
+    if (K > 0) list_topk(sm, list, a.nchunks, K);
 
     if ((tid >> 6) != 0) return;
     const int lane = lane_id();

@@ -41,7 +41,7 @@ __device__ __forceinline__ float penalize(float v, uint32_t c, float rep, float 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int EPT, bool VEC>
-__global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
+__global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const SampleArgs a)
 {
     constexpr int CH = EPT * kBlock;
     constexpr int NQ = EPT / 4;
@@ -55,14 +55,15 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
     const int n_eff = (int)(R.pack & 0xFFFFu);
     const int k = (int)((R.pack >> 16) & 0x7Fu);
     const bool greedy = ((R.pack >> 24) & 1u) != 0u;
-    const int64_t base = (int64_t)chunk * CH;
+    const int base = chunk * CH;
     const float *x = a.logits + (int64_t)slot * a.ld;
 
-    // Issue every load of the chunk first; the bitmap build below overlaps them.
+    // Issue every load of the chunk first; the bitmap build below overlaps
+    // them.  Ids past V (only in the last chunk) read as NaN: never selected.
     float v[EPT];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        const int64_t i0 = base + q * 1024 + tid * 4;
+        const int i0 = base + q * 1024 + tid * 4;
         if (VEC && i0 + 4 <= V) {
             const f32x4 t = *reinterpret_cast<const f32x4 *>(x + i0);
             v[4 * q + 0] = t.x;
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
             v[4 * q + 3] = t.w;
         } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) v[4 * q + s] = (i0 + s < V) ? x[i0 + s] : 0.0f;
+            for (int s = 0; s < 4; ++s)
+                v[4 * q + s] = (i0 + s < V) ? x[i0 + s] : __builtin_nanf("");
         }
     }
 
@@ -82,22 +84,16 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
         const int32_t *h = a.history + R.hist_off;
         for (int j = tid; j < n_eff; j += kBlock) {
             const int32_t id = h[j];
-            const int64_t rel = (int64_t)id - base;
+            const int rel = id - base;
             if (id >= 0 && id < V && rel >= 0 && rel < CH) {
                 atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
                 atomicAdd(&sm.pen_cnt[rel >> 1], 1u << ((rel & 1) * 16));
             }
         }
         __syncthreads();
-    }
-
+        // Only flagged ids look up a count; they leave sanitised.
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int64_t i0 = base + q * 1024 + tid * 4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            v[4 * q + s] = (i0 + s < V) ? sanitize(v[4 * q + s]) : __builtin_nanf("");
-        if (n_eff > 0) {
+        for (int q = 0; q < NQ; ++q) {
             const int rel = q * 1024 + tid * 4;
             const uint32_t nib = (sm.pen_bits[rel >> 5] >> (rel & 31)) & 0xFu;
             if (nib) {
@@ -106,7 +102,7 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
                     if ((nib >> s) & 1u) {
                         const int r = rel + s;
                         const uint32_t c = (sm.pen_cnt[r >> 1] >> ((r & 1) * 16)) & 0xFFFFu;
-                        v[4 * q + s] = penalize(v[4 * q + s], c, R.rep, R.freq, R.present);
+                        v[4 * q + s] = penalize(sanitize(v[4 * q + s]), c, R.rep, R.freq, R.present);
                     }
                 }
             }
@@ -114,12 +110,12 @@ __global__ __launch_bounds__(kBlock) void sample_kernel(const SampleArgs a)
     }
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    chunk_topk<EPT>(sm.s, v, base, k, list + (int64_t)chunk * k);
+    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k);
 
     if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.s.flag)) return;
 
     // ---- the last workgroup of the row: merge, then the cuts and the draw.
-    list_topk(sm.s, list, a.nchunks * k, k);
+    list_topk(sm.s, list, a.nchunks, k);
 
     if ((tid >> 6) != 0) return;
     const int lane = lane_id();

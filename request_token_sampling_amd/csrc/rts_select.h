@@ -124,34 +124,51 @@ __device__ __forceinline__ uint64_t block_max_u64(SelectSmem &sm, uint64_t v)
     return m;
 }
 
-// Chunk selection over register-resident values.  v[e] holds the (already
-// transformed) value of element idx = base + (e/4)*1024 + tid*4 + e%4, or NaN
-// for "no element".  Writes the chunk's top-k keys in order to out[0..k).
+// Chunk selection over register-resident values.  v[e] holds the value of
+// element idx = base + (e/4)*1024 + tid*4 + e%4; ids >= V hold NaN.  Values
+// may be raw: NaN stands for -inf and +inf for the largest float, and both
+// are mapped when a key is formed.  Writes the chunk's top-k keys in order to
+// out[0..k).
 template <int EPT>
-__device__ __forceinline__ void chunk_topk(SelectSmem &sm, const float (&v)[EPT], int64_t base,
-                                           int k, uint64_t *out_keys)
+__device__ __forceinline__ uint32_t elem_index(int base, int e)
+{
+    return (uint32_t)(base + (e >> 2) * 1024 + (int)threadIdx.x * 4 + (e & 3));
+}
+
+template <int EPT>
+__device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int base, int V, int k,
+                                           uint64_t *out_keys)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const ToWorkspace out{out_keys};
+    constexpr float kFltMax = 3.40282346638528859812e+38f;
 
+    // fmaxf skips NaN, so the lane maximum is over the non-NaN values.
     float lmax = __builtin_nanf("");
 #pragma unroll
     for (int e = 0; e < EPT; ++e) lmax = fmaxf(lmax, v[e]);
+    lmax = (lmax == lmax) ? fminf(lmax, kFltMax) : lmax;  // fminf would turn NaN into FLT_MAX
 
     if (k == 1) {
         // Argmax: the lane's first element equal to its maximum (elements are
         // in increasing index order), then a block maximum of the keys.
-        int first = 0;
-#pragma unroll
-        for (int e = EPT - 1; e >= 0; --e) first = (v[e] == lmax) ? e : first;
+        // Lanes whose maximum is -inf or empty offer nothing here; if every
+        // lane is like that the general path below handles the chunk.
         uint64_t key = 0;
+        if (lmax == lmax && lmax > -INFINITY) {
+            int first = 0;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            if (e == first && lmax == lmax)
-                key = cand_key(lmax, (uint32_t)(base + (e >> 2) * 1024 + tid * 4 + (e & 3)));
-        key = block_max_u64(sm, key);
-        if (tid == 0) out.put(0, key);
-        return;
+            for (int e = EPT - 1; e >= 0; --e)
+                first = (v[e] == v[e] && fminf(v[e], kFltMax) == lmax) ? e : first;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (e == first) key = cand_key(lmax, elem_index<EPT>(base, e));
+        }
+        key = block_max_u64(sm, key);  // every thread of the block takes part
+        if (key != 0ull) {
+            if (tid == 0) out.put(0, key);
+            return;
+        }
     }
 
     sm.lane_keys[tid] = (lmax != lmax) ? 0u : value_key(lmax);
@@ -160,6 +177,13 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, const float (&v)[EPT]
     const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                             sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
     const float tf = key_threshold(kth_largest_key_256<16>(lk, k));
+    if (tf == -INFINITY) {
+        // Degenerate chunk (fewer than k values above -inf): every id below V
+        // is a candidate, NaN counting as -inf.
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            v[e] = ((int)elem_index<EPT>(base, e) < V) ? sanitize(v[e]) : __builtin_nanf("");
+    }
 
     const uint64_t below = lanes_below_mask();
     uint64_t *wc = sm.cand + wave * kCap;
@@ -171,7 +195,7 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, const float (&v)[EPT]
         if (m) {
             const uint32_t pos = wcnt + (uint32_t)__popcll(m & below);
             if (c && pos < (uint32_t)kCap)
-                wc[pos] = cand_key(v[e], (uint32_t)(base + (e >> 2) * 1024 + tid * 4 + (e & 3)));
+                wc[pos] = cand_key(fminf(v[e], kFltMax), elem_index<EPT>(base, e));
             wcnt += (uint32_t)__popcll(m);
         }
     }
@@ -190,9 +214,9 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, const float (&v)[EPT]
         uint64_t best = 0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            if (v[e] == v[e]) {
-                const uint64_t key =
-                    cand_key(v[e], (uint32_t)(base + (e >> 2) * 1024 + tid * 4 + (e & 3)));
+            const uint32_t idx = elem_index<EPT>(base, e);
+            if ((int)idx < V) {
+                const uint64_t key = cand_key(sanitize(v[e]), idx);
                 best = (key < prev && key > best) ? key : best;
             }
         }
@@ -202,37 +226,74 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, const float (&v)[EPT]
     }
 }
 
-// Top-k of a list of n published keys (0 = no element), written in order to
-// sm.sel[0..k).  Used by the row merge.  The first kCache keys of every thread
-// are loaded in one batch and kept in registers; longer lists are re-read in
-// batches of the same size.  Ends after a barrier.
-constexpr int kCache = 16;
+// Row merge: top-k of the chunk lists, written in order to sm.sel[0..k).
+// Chunk c published its top-k keys in descending order at list[c*k ..
+// c*k + k), zero-padded.  The lists are read as sorted streams: with C <= 256
+// chunks, lane (c, g) owns chunk c's ranks g, g + G, g + 2G, ... where
+// G = 256 / C, so the lane's maximum is its first key and the 256 lane maxima
+// are the top ranks of every chunk; the k-th largest of them is then close to
+// the row's k-th key.  With more chunks each lane owns whole chunks t, t + 256,
+// ...  A lane stops reading a stream at its first key below the threshold.
+// Loads are device-coherent and issued eight at a time.  Ends after a barrier.
+constexpr int kBatch = 8;
 
-__device__ __forceinline__ void load_batch(const uint64_t *list, int n, int first,
-                                           uint64_t (&kv)[kCache])
+struct MergeStreams {
+    int G;        // rank stride inside a stream
+    int g;        // first rank
+    int c0;       // first chunk of the lane
+    int cstride;  // chunk stride between the lane's streams
+    int nstreams; // streams of this lane
+    int max_streams;
+};
+
+__device__ __forceinline__ MergeStreams merge_streams(int C, int k)
 {
+    const int t = threadIdx.x;
+    MergeStreams m;
+    if (C <= kBlock) {
+        m.G = kBlock / C;
+        m.g = t / C;
+        m.c0 = t % C;
+        m.cstride = 0;
+        m.nstreams = (t < m.G * C && m.g < k) ? 1 : 0;
+        m.max_streams = 1;
+    } else {
+        m.G = 1;
+        m.g = 0;
+        m.c0 = t;
+        m.cstride = kBlock;
+        m.nstreams = (C - t + kBlock - 1) / kBlock;
+        m.max_streams = (C + kBlock - 1) / kBlock;
+    }
+    return m;
+}
+
+__device__ __forceinline__ void load_stream_batch(const uint64_t *list, int k, const MergeStreams &m,
+                                                  int c, bool has, int j0, uint64_t (&kv)[kBatch])
+{
+    const int L = (k - m.g + m.G - 1) / m.G;  // keys in the stream
 #pragma unroll
-    for (int i = 0; i < kCache; ++i) {
-        const int f = first + i * kBlock + (int)threadIdx.x;
-        kv[i] = (f < n) ? read_published_u64(list + f) : 0ull;
+    for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + u;
+        kv[u] = (has && j < L) ? read_published_u64(list + (int64_t)c * k + m.g + m.G * j) : 0ull;
     }
 }
 
-__device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, int n, int k)
+__device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, int C, int k)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    constexpr int kSpan = kCache * kBlock;
+    const MergeStreams ms = merge_streams(C, k);
 
-    uint64_t kr[kCache];
-    load_batch(list, n, 0, kr);
-    uint64_t lm = 0;
-#pragma unroll
-    for (int i = 0; i < kCache; ++i) lm = kr[i] > lm ? kr[i] : lm;
-    for (int first = kSpan; first < n; first += kSpan) {
-        uint64_t t[kCache];
-        load_batch(list, n, first, t);
-#pragma unroll
-        for (int i = 0; i < kCache; ++i) lm = t[i] > lm ? t[i] : lm;
+    // pass 1: the first batch of the first stream (kept), heads of the others
+    uint64_t first[kBatch];
+    load_stream_batch(list, k, ms, ms.c0, ms.nstreams > 0, 0, first);
+    uint64_t lm = first[0];
+    for (int si = 1; si < ms.max_streams; ++si) {
+        const int c = ms.c0 + si * ms.cstride;
+        if (si < ms.nstreams) {
+            const uint64_t h = read_published_u64(list + (int64_t)c * k);
+            lm = h > lm ? h : lm;
+        }
     }
     if (k == 1) {
         lm = block_max_u64(sm, lm);
@@ -246,26 +307,34 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
                             sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
     const uint64_t t64 = (uint64_t)kth_largest_key_256<16>(lk, k) << 32;
 
+    // pass 2: walk every stream while its keys reach the threshold
     const uint64_t below = lanes_below_mask();
     uint64_t *wc = sm.cand + wave * kCap;
     uint32_t wcnt = 0;
-    auto compact = [&](const uint64_t (&kv)[kCache]) {
+    for (int si = 0; si < ms.max_streams; ++si) {
+        const int c = ms.c0 + si * ms.cstride;
+        bool live = si < ms.nstreams;
+        for (int j0 = 0; __ballot(live) != 0ull; j0 += kBatch) {
+            uint64_t kv[kBatch];
+            if (si == 0 && j0 == 0) {
 #pragma unroll
-        for (int i = 0; i < kCache; ++i) {
-            const bool c = kv[i] != 0ull && kv[i] >= t64;
-            const uint64_t m = __ballot(c);
-            if (m) {
-                const uint32_t pos = wcnt + (uint32_t)__popcll(m & below);
-                if (c && pos < (uint32_t)kCap) wc[pos] = kv[i];
-                wcnt += (uint32_t)__popcll(m);
+                for (int u = 0; u < kBatch; ++u) kv[u] = first[u];
+            } else {
+                load_stream_batch(list, k, ms, c, live, j0, kv);
             }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const bool cnd = live && kv[u] != 0ull && kv[u] >= t64;
+                const uint64_t m = __ballot(cnd);
+                if (m) {
+                    const uint32_t pos = wcnt + (uint32_t)__popcll(m & below);
+                    if (cnd && pos < (uint32_t)kCap) wc[pos] = kv[u];
+                    wcnt += (uint32_t)__popcll(m);
+                }
+            }
+            // descending stream: it ends at its first key below the threshold
+            live = live && kv[kBatch - 1] != 0ull && kv[kBatch - 1] >= t64;
         }
-    };
-    compact(kr);
-    for (int first = kSpan; first < n; first += kSpan) {
-        uint64_t t[kCache];
-        load_batch(list, n, first, t);
-        compact(t);
     }
     if (lane == 0) sm.wave_cnt[wave] = wcnt;
     pad_region(sm, wave, wcnt);
@@ -276,14 +345,20 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
         __syncthreads();
         return;
     }
+    // Fallback (massive ties): k argmax rounds over the whole list.
+    const int n = C * k;
     uint64_t prev = ~0ull;
     for (int r = 0; r < k; ++r) {
         uint64_t best = 0;
-        for (int first = 0; first < n; first += kSpan) {
-            uint64_t t[kCache];
-            load_batch(list, n, first, t);
+        for (int f0 = 0; f0 < n; f0 += kBatch * kBlock) {
+            uint64_t t[kBatch];
 #pragma unroll
-            for (int i = 0; i < kCache; ++i) best = (t[i] < prev && t[i] > best) ? t[i] : best;
+            for (int u = 0; u < kBatch; ++u) {
+                const int f = f0 + u * kBlock + tid;
+                t[u] = (f < n) ? read_published_u64(list + f) : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) best = (t[u] < prev && t[u] > best) ? t[u] : best;
         }
         best = block_max_u64(sm, best);
         if (tid == 0) sm.sel[r] = best;

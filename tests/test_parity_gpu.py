@@ -130,6 +130,28 @@ def test_special_values():
     check(x, params, tag="special")
 
 
+@pytest.mark.parametrize("Vx", [1030, 20000, V])
+def test_nan_lanes_beside_flt_max(Vx):
+    """Lanes whose values are all NaN (or past V) next to lanes holding
+    FLT_MAX / +inf: NaN counts as -inf and never takes part in a maximum;
+    greedy rows and sampled rows both."""
+    rng = np.random.default_rng(Vx + 3)
+    x = rng.normal(0, 3, (4, Vx)).astype(np.float32)
+    x[0, :700] = np.nan
+    x[0, 5] = np.inf
+    x[0, 900 % Vx] = np.float32(3.4028235e38)
+    x[1, ::2] = np.nan
+    x[1, 1::97] = np.inf
+    x[2] = np.nan
+    x[2, -1] = -np.inf
+    x[3] = -np.inf
+    x[3, ::5] = np.nan
+    params = [W.row_params(), sampled(top_k=3, counter=1), W.row_params(),
+              sampled(top_k=64, counter=2)]
+    check(x, params, tag=f"nan lanes V={Vx}")
+    check(x, [sampled(top_k=1, counter=r) for r in range(4)], tag=f"nan lanes k=1 V={Vx}")
+
+
 def test_all_equal_rows_force_fallbacks():
     """Every logit equal: each chunk's candidate buffer overflows (k rounds
     over registers) and so does the row merge (k rounds over the list)."""
