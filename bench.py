@@ -1,6 +1,8 @@
 """Benchmark of the per-token sampler on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single_stream|window|batch|stress]
+python bench.py --summarize-trace KERNEL_STATS_CSV --workload W --cmd "..."
+python bench.py --summarize-pmc FETCH_CSV WRITE_CSV --workload W --cmd "..."
 
 A step is one pass of the hot path over one batch of the workload:
   single_stream  one row of 248,320 fp32 logits, the sampled chain (top_k 20,
@@ -42,6 +44,11 @@ def parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads' figures in the JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain 256 MiB device copy (known bytes) for counter scaling")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--cmd", default="", help="profiling command recorded in the summary")
     return ap.parse_args()
 
 
@@ -183,6 +190,100 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+COPY_BYTES = 256 << 20
+
+
+def calibration_copy(dev):
+    """A plain device-to-device copy of COPY_BYTES, three times: the HBM
+    counters of these dispatches calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(path, workload, cmd):
+    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    rows = _csv_rows(path)
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command: {cmd}",
+             f"# summarised by: python bench.py --summarize-trace {os.path.basename(path)} "
+             f"--workload {workload}",
+             "kernel | calls | average_us | min_us | max_us | percent"]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or ""
+        if not name:
+            continue
+        def us(key):
+            v = r.get(key)
+            return f"{float(v) / 1000:.3f}" if v not in (None, "") else "-"
+        lines.append(f"{name[:90]} | {r.get('Calls', '-')} | {us('AverageNs')} | {us('MinNs')} | "
+                     f"{us('MaxNs')} | {float(r.get('Percentage', 0)):.2f}")
+    out = os.path.join(PROFILES, f"sample_kernel_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, cmd):
+    """HBM bytes per sampler launch from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the calibration copy of COPY_BYTES."""
+    import statistics
+
+    def per_kernel(path, counter):
+        """Counter values of the sampler dispatches, and of the first three
+        copy dispatches of the run: the calibration copies, which run before
+        anything else copies on the device."""
+        sample, copies = [], []
+        for r in _csv_rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            if "rts::sample_kernel" in name:
+                sample.append(val)
+            elif "copy" in name.lower():
+                copies.append((int(r["Dispatch_Id"]), val))
+        copies.sort()
+        return {"sample": sample, "copy": [v for _, v in copies[:3]]}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    f_copy, w_copy = statistics.median(f["copy"]), statistics.median(w["copy"])
+    f_scale = COPY_BYTES / (f_copy * 1024.0)
+    w_scale = COPY_BYTES / (w_copy * 1024.0)
+    f_s, w_s = statistics.median(f["sample"]), statistics.median(w["sample"])
+    fetch_b, write_b = f_s * 1024.0 * f_scale, w_s * 1024.0 * w_scale
+    lines = [f"# HBM traffic of rts::sample_kernel, workload {workload}",
+             f"# command (FETCH_SIZE pass, then WRITE_SIZE pass): {cmd}",
+             f"# summarised by: python bench.py --summarize-pmc {os.path.basename(fetch_csv)} "
+             f"{os.path.basename(write_csv)} --workload {workload}",
+             f"# calibration: a {COPY_BYTES} B device copy reads FETCH_SIZE {f_copy:.1f} KiB and "
+             f"writes WRITE_SIZE {w_copy:.1f} KiB per dispatch",
+             f"fetch_scale = {f_scale:.4f}",
+             f"write_scale = {w_scale:.4f}",
+             f"sample_dispatches = {len(f['sample'])}",
+             f"fetch_kib_per_launch_raw = {f_s:.1f}",
+             f"write_kib_per_launch_raw = {w_s:.1f}",
+             f"fetch_bytes_per_launch = {fetch_b:.0f}",
+             f"write_bytes_per_launch = {write_b:.0f}",
+             f"hbm_bytes_per_launch = {fetch_b + write_b:.0f}",
+             f"source_sha256 = {kernel_source_hash()}"]
+    out = os.path.join(PROFILES, f"traffic_sample_kernel_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
 def cpu_baseline(seconds):
     """The oracle as it stands, single-threaded, on the single-stream row
     (sampled pass plus greedy pass, as one GPU step), for about `seconds`."""
@@ -209,6 +310,12 @@ def progress(msg):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.cmd)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.cmd)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the sampler's rows are independent and this "
               "build runs on a single MI355X; run it with --gpus 1.", file=sys.stderr)
@@ -218,6 +325,8 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
 
+    if args.calibration_copy:
+        calibration_copy(dev)
     wl = Workload(args.workload, dev)
     progress(f"{args.workload}: {wl.ncopies} copies resident, timing {args.steps} steps")
     wall, kern_ms = time_workload(wl, args.steps, args.warmup)
