@@ -13,7 +13,10 @@ A step is one pass of the hot path over one batch of the workload:
                  unrestricted and over 1,000 allowed ids per row.
 Logits are resident in HBM before timing.  Each step reads a different copy of
 the batch, rotating through at least 512 MiB of copies, so the reads come
-from HBM and not from the 256 MiB MALL.  Prints one JSON line.
+from HBM and not from the 256 MiB MALL.  The timed steps are captured once
+in a HIP graph and replayed (Philox counters live in device memory and
+advance on every call, so replays draw fresh numbers); an eager timing, where
+Python launches every call, is reported beside it.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -54,7 +57,9 @@ def parse():
 
 # ---------------------------------------------------------------- workloads
 class Workload:
-    """Device-resident copies of one batch plus the calls of one step."""
+    """Device-resident copies of one batch plus the prepared calls of one step.
+    Philox counters are device-resident and advance on every call, so steps
+    captured in a HIP graph draw fresh numbers on every replay."""
 
     def __init__(self, name, dev):
         import numpy as np
@@ -64,14 +69,12 @@ class Workload:
         from request_token_sampling_amd import workloads as W
 
         self.name = name
-        self.passes = []          # list of (label, params array, rows_counted_as_sampled)
-        self.logprob = None
         hist = hist_len = None
+        lp = None
         if name == "single_stream":
             w = W.single_stream()
             x = w["logits"]
-            self.passes = [("sampled", R.row_params(w["sampled"]), 1),
-                           ("greedy", R.row_params(w["greedy"]), 0)]
+            passes = [("sampled", w["sampled"], 1, 1), ("greedy", w["greedy"], 0, 1)]
             self.desc = ("single stream: 1 row, V=248,320 fp32 N(0,3) with 3 spiked heads; "
                          "top_k 20, top_p 0.8, min_p 0, temperature 0.7, no penalties; "
                          "plus a greedy pass over the same row")
@@ -80,21 +83,21 @@ class Workload:
             x = vw.next_logits()
             hist = vw.history.reshape(1, -1)
             hist_len = [hist.shape[1]]
-            self.passes = [("sampled", R.row_params(vw.params(0)), 5)]
+            passes = [("sampled", vw.params(0), 5, 5)]
             self.desc = ("verify window: 5 rows, V=248,320, penalties 1.1/0.5/0.5 over a "
                          "64-id history, top_k 40, min_p 0.05, top_p 0.95, temperature 1")
         elif name == "batch":
             w = W.batch_slots()
             x, hist, hist_len = w["logits"], w["history"], w["hist_len"]
-            self.passes = [("sampled", R.row_params(w["params"]), 40)]
+            passes = [("sampled", w["params"], 40, 5)]
             self.desc = ("batch slots: 40 rows, V=248,320, per-row T/top_k/top_p/min_p, "
                          "penalties over 256 Zipf history ids per slot")
         else:
             w = W.logprobs_stress()
             x = w["logits"]
-            self.passes = [("sampled", R.row_params(w["params"]), 40)]
+            passes = [("sampled", w["params"], 40, 40)]
             ids, off = W.pack_allowed(w["allowed"])
-            self.logprob = (w["top_n"], torch.from_numpy(ids).to(dev), off)
+            lp = (w["top_n"], ids, off)
             self.desc = ("logprobs stress: 40 bf16-grid rows, V=248,320, top_k 64, min_p 0.1; "
                          "top-20 logprobs unrestricted and over 1,000 allowed ids per row")
         self.B, self.V = x.shape
@@ -104,14 +107,27 @@ class Workload:
         base = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         self.copies = base.unsqueeze(0).repeat(self.ncopies, 1, 1)
         self.hist = None if hist is None else torch.from_numpy(np.asarray(hist, np.int32)).to(dev)
-        self.hist_len = hist_len
         self.ws = R.make_workspace(self.B, self.V, dev)
-        stream = torch.cuda.current_stream()
-        self.calls = [R.SampleCall(self.copies[0], p, self.hist, hist_len, workspace=self.ws,
-                                   stream=stream) for _, p, _ in self.passes]
-        self.sampled_rows = sum(n for _, _, n in self.passes)
-        self.tokens = self.calls[0].token
-        self.R = R
+        self.calls, self.labels = [], []
+        self.sampled_rows = 0
+        for label, params, counted, stride in passes:
+            ctr = torch.tensor([p.get("counter", 0) for p in params], dtype=torch.int64,
+                               device=dev)
+            self.calls.append(R.SampleCall(self.copies[0], params, self.hist, hist_len,
+                                           workspace=self.ws, counters=ctr,
+                                           counter_stride=stride))
+            self.labels.append(label)
+            self.sampled_rows += counted
+        self.lp_calls = []
+        if lp is not None:
+            top_n, ids, off = lp
+            tok = self.calls[0].token
+            self.lp_calls = [R.LogprobCall(self.copies[0], tok, top_n, workspace=self.ws),
+                             R.LogprobCall(self.copies[0], tok, top_n,
+                                           torch.from_numpy(ids).to(dev), off,
+                                           workspace=self.ws)]
+        self.passes = [l for l in self.labels] + (["logprobs", "logprobs_allowed"]
+                                                  if self.lp_calls else [])
         self.torch = torch
 
     def step(self, i, events=None):
@@ -123,42 +139,81 @@ class Workload:
             c()
             if events is not None:
                 events[j][1].record()
-        if self.logprob is not None:
-            top_n, ids, off = self.logprob
-            self.R.token_logprobs(x, self.tokens, top_n, workspace=self.ws)
-            self.R.token_logprobs(x, self.tokens, top_n, ids, off, workspace=self.ws)
+        for c in self.lp_calls:
+            c.logits = x
+            c()
 
 
-def time_workload(wl, steps, warmup):
-    """Wall time of `steps` steps, and the average HIP-event duration of each
-    sampler call (events recorded on the stream the kernels run on)."""
+def time_eager(wl, steps, warmup):
+    """Wall time of `steps` eager steps (Python launches each call)."""
     torch = wl.torch
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(warmup + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_graph(wl, steps):
+    """Wall time of `steps` steps replayed from one captured HIP graph."""
+    torch = wl.torch
+    wl.step(0)                      # eager warm-up of every kernel variant
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            wl.step(i)
+    torch.cuda.synchronize()
+    graph.replay()                  # warm-up replay
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    return wall
+
+
+def kernel_durations(wl, steps):
+    """Average duration of each sampler call from HIP events recorded around
+    it on its launch stream.  The stream is first held by a sleep kernel so
+    the host enqueues ahead: the events then bracket the kernels themselves,
+    not the host's launch latency."""
+    torch = wl.torch
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)] for _ in wl.calls]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(steps * 0.08e-3 * 2.0e9))
     for i in range(steps):
-        wl.step(warmup + i, [(e[i][0], e[i][1]) for e in ev])
+        wl.step(i, [(e[i][0], e[i][1]) for e in ev])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [sum(a.elapsed_time(b) for a, b in e) / steps for e in ev]
-    return wall, kern_ms
+    return [sum(a.elapsed_time(b) for a, b in e) / steps for e in ev]
 
 
 def roofline(wl, kern_ms):
-    """HBM roofline of the sampled-chain kernel: algorithmic bytes per launch
-    (one read of every logit row, plus outputs) over its average duration."""
-    out_bytes = wl.B * (4 + 12 + 256 + 256 + 4)
+    """HBM roofline of the sampler kernel: algorithmic bytes per launch (one
+    read of every logit row, plus outputs) over its average launch duration
+    (all sampler launches of a step: they are one kernel)."""
+    out_bytes = wl.B * (4 + 12 + 256 + 256 + 4 + 8)
     alg = wl.B * wl.row_bytes + out_bytes
-    dur_s = kern_ms[0] * 1e-3
-    achieved = alg / dur_s / 1e9
+    avg_ms = sum(kern_ms) / len(kern_ms)
+    achieved = alg / (avg_ms * 1e-3) / 1e9
     return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=read_traffic(wl.name),
-                kernel="sample_kernel", algorithmic_bytes_per_launch=alg,
-                avg_launch_us=round(kern_ms[0] * 1e3, 3))
+                kernel="rts::sample_kernel", algorithmic_bytes_per_launch=alg,
+                avg_launch_us=round(avg_ms * 1e3, 3),
+                per_call_us={l: round(m * 1e3, 3) for l, m in zip(wl.labels, kern_ms)})
+
+
+def measure(wl, steps, warmup):
+    eager = time_eager(wl, steps, warmup)
+    graph = time_graph(wl, steps)
+    kern = kernel_durations(wl, min(steps, 500))
+    return dict(graph_wall=graph, eager_wall=eager, kern_ms=kern)
 
 
 def read_traffic(workload):
@@ -329,10 +384,10 @@ def main():
         calibration_copy(dev)
     wl = Workload(args.workload, dev)
     progress(f"{args.workload}: {wl.ncopies} copies resident, timing {args.steps} steps")
-    wall, kern_ms = time_workload(wl, args.steps, args.warmup)
-    progress(f"{args.workload}: {wall / args.steps * 1e3:.4f} ms/step, kernels {kern_ms}")
-    ms_step = wall / args.steps * 1e3
-    value = wl.sampled_rows * args.steps / wall
+    m = measure(wl, args.steps, args.warmup)
+    progress(f"{args.workload}: graph {m['graph_wall'] / args.steps * 1e3:.4f} ms/step, eager "
+             f"{m['eager_wall'] / args.steps * 1e3:.4f} ms/step, kernels {m['kern_ms']}")
+    value = wl.sampled_rows * args.steps / m["graph_wall"]
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -340,18 +395,19 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(m["graph_wall"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.desc, "rows_per_step": wl.B, "V": wl.V,
-                   "passes_per_step": [p[0] for p in wl.passes] +
-                   (["logprobs", "logprobs_allowed"] if wl.logprob else []),
+                   "passes_per_step": wl.passes, "launch": "hip_graph_replay",
+                   "philox_counters": "device-resident, advanced per call",
                    "logit_copies_rotated": wl.ncopies, "device": props.name},
-        "roofline": roofline(wl, kern_ms),
-        "kernel_us_per_call": [round(m * 1e3, 3) for m in kern_ms],
+        "roofline": roofline(wl, m["kern_ms"]),
+        "eager": {"value": round(wl.sampled_rows * args.steps / m["eager_wall"], 1),
+                  "ms_per_step": round(m["eager_wall"] / args.steps * 1e3, 5)},
     }
     if not args.no_extra:
         extra = {}
@@ -360,11 +416,15 @@ def main():
                 continue
             w2 = Workload(name, dev)
             steps = max(50, args.steps // 4)
-            wall2, k2 = time_workload(w2, steps, max(10, args.warmup // 4))
-            progress(f"{name}: {wall2 / steps * 1e3:.4f} ms/step, kernels {k2}")
-            extra[name] = dict(value=round(w2.sampled_rows * steps / wall2, 1), unit="rows/s",
-                               ms_per_step=round(wall2 / steps * 1e3, 5),
-                               roofline=roofline(w2, k2), desc=w2.desc)
+            m2 = measure(w2, steps, max(10, args.warmup // 4))
+            progress(f"{name}: graph {m2['graph_wall'] / steps * 1e3:.4f} ms/step, kernels "
+                     f"{m2['kern_ms']}")
+            extra[name] = dict(value=round(w2.sampled_rows * steps / m2["graph_wall"], 1),
+                               unit="rows/s", steps=steps,
+                               ms_per_step=round(m2["graph_wall"] / steps * 1e3, 5),
+                               eager_ms_per_step=round(m2["eager_wall"] / steps * 1e3, 5),
+                               roofline=roofline(w2, m2["kern_ms"]), desc=w2.desc,
+                               passes_per_step=w2.passes)
             del w2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra

@@ -94,6 +94,14 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
  *   kept_ids    int32 [B][64]  the top_k sequence, padded with -1.
  *   kept_logits f32 [B][64]    its penalised logits, padded with -inf.
  *   philox_x0   uint32 [B]     first Philox output word (0 for greedy rows).
+ *   counters    device uint64 [B] or NULL.  NULL: row r draws with
+ *               params[r].counter.  Otherwise row r draws with counters[r]
+ *               (params[r].counter is ignored) and the call adds
+ *               counter_stride to counters[r] (every row, greedy ones too),
+ *               so a captured HIP graph that replays the call draws fresh
+ *               numbers on every replay instead of repeating them (page
+ *               "#19 ...", "Problem": a captured sampler would replay the same
+ *               draws forever; "A persistent per-request draw counter").
  * Errors: RTS_EINVAL for B < 0, V out of range, ld < V, NULL logits/token,
  * a row with NaN or infinite temperature, top_k outside 1..64 on a sampled
  * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
@@ -107,6 +115,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       const int32_t *history_len,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
+                      uint64_t *counters, int64_t counter_stride,
                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
         L.rts_workspace_bytes.argtypes = [I64, I64, ctypes.POINTER(ctypes.c_size_t)]
         L.rts_workspace_init.argtypes = [P, SZ, P]
         L.rts_sample_tokens.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P, P, P,
-                                        SZ, P]
+                                        I64, P, SZ, P]
         L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
                   "rts_token_logprobs"):
@@ -137,7 +137,7 @@ class SampleCall:
     with ``set_params``."""
 
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
-                 stream=None):
+                 stream=None, counters=None, counter_stride=0):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -154,6 +154,11 @@ class SampleCall:
             self.hist_len = np.ascontiguousarray(history_len, dtype=np.int32)
         else:
             self.H, self.ldh, self.hist_len = 0, 0, None
+        if counters is not None:
+            if counters.dtype != torch.int64 or not counters.is_cuda or counters.numel() < self.B:
+                raise ValueError("counters must be a CUDA int64 tensor with one entry per row")
+        self.counters = counters
+        self.counter_stride = int(counter_stride)
         self.set_params(params)
         self.stream = stream
 
@@ -167,14 +172,15 @@ class SampleCall:
             _ptr(self.history), self.H, self.ldh,
             None if self.hist_len is None else self.hist_len.ctypes.data_as(ctypes.c_void_p),
             _ptr(self.token), _ptr(self.counts), _ptr(self.kept_ids), _ptr(self.kept_logits),
-            _ptr(self.philox_x0), _ptr(self.workspace), self.workspace.numel(), None]
+            _ptr(self.philox_x0), _ptr(self.counters), self.counter_stride,
+            _ptr(self.workspace), self.workspace.numel(), None]
 
     def __call__(self):
         if self._args is None:
             self._build_args()
         a = self._args
         a[0] = self.logits.data_ptr()
-        a[16] = _stream_handle(self.stream)
+        a[18] = _stream_handle(self.stream)
         _check(lib().rts_sample_tokens(*a))
         return self
 
@@ -185,39 +191,66 @@ class SampleCall:
 
 
 def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
-                  stream=None) -> dict:
+                  stream=None, counters=None, counter_stride=0) -> dict:
     """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
 
     params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
     history: CUDA int32 [H][ldh] with host lengths history_len[H], or None.
     Returns device tensors token[B], counts[B][3], kept_ids[B][64],
-    kept_logits[B][64], philox_x0[B]."""
-    return SampleCall(logits, params, history, history_len, workspace, stream)().results()
+    kept_logits[B][64], philox_x0[B].  counters: optional CUDA int64 [B]
+    device-resident Philox counters, advanced by counter_stride per call."""
+    return SampleCall(logits, params, history, history_len, workspace, stream, counters,
+                      counter_stride)().results()
+
+
+class LogprobCall:
+    """One prepared call of rts_token_logprobs (outputs, workspace and ctypes
+    arguments built once; the tokens tensor is read at each call)."""
+
+    def __init__(self, logits, tokens, top_n: int, allowed=None, allowed_off=None,
+                 workspace=None, stream=None):
+        self.logits, self.B, self.V, self.ld = _rows_view(logits)
+        dev = self.logits.device
+        if tokens.dtype != torch.int32 or not tokens.is_cuda:
+            raise ValueError("tokens must be a CUDA int32 tensor")
+        self.tokens = tokens
+        self.top_n = int(top_n)
+        self.token_lp = torch.empty(self.B, dtype=torch.float32, device=dev)
+        self.top_ids = torch.empty((self.B, max(self.top_n, 0)), dtype=torch.int32, device=dev)
+        self.top_lp = torch.empty((self.B, max(self.top_n, 0)), dtype=torch.float32, device=dev)
+        self.workspace = workspace if workspace is not None else make_workspace(self.B, self.V,
+                                                                                dev)
+        self.allowed = allowed
+        self.off = None if allowed is None else np.ascontiguousarray(allowed_off, dtype=np.int64)
+        self.stream = stream
+        self._args = None
+
+    def __call__(self):
+        if self._args is None:
+            self._args = [
+                None, self.B, self.V, self.ld, None, self.top_n, _ptr(self.allowed),
+                None if self.off is None else self.off.ctypes.data_as(ctypes.c_void_p),
+                _ptr(self.token_lp), _ptr(self.top_ids) if self.top_n > 0 else None,
+                _ptr(self.top_lp) if self.top_n > 0 else None, _ptr(self.workspace),
+                self.workspace.numel(), None]
+        a = self._args
+        a[0] = self.logits.data_ptr()
+        a[4] = self.tokens.data_ptr()
+        a[13] = _stream_handle(self.stream)
+        _check(lib().rts_token_logprobs(*a))
+        return self
+
+    def results(self) -> dict:
+        return dict(token_lp=self.token_lp, top_ids=self.top_ids, top_lp=self.top_lp)
 
 
 def token_logprobs(logits, tokens, top_n: int, allowed=None, allowed_off=None,
                    workspace=None, stream=None) -> dict:
     """Raw-logit log-softmax per row: token_lp[B], top_ids[B][top_n],
     top_lp[B][top_n].  allowed: CUDA int32 ids with host int64 offsets [B+1]."""
-    logits, B, V, ld = _rows_view(logits)
-    dev = logits.device
-    if tokens.dtype != torch.int32 or not tokens.is_cuda:
-        raise ValueError("tokens must be a CUDA int32 tensor")
-    token_lp = torch.empty(B, dtype=torch.float32, device=dev)
-    top_ids = torch.empty((B, max(top_n, 0)), dtype=torch.int32, device=dev)
-    top_lp = torch.empty((B, max(top_n, 0)), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else make_workspace(B, V, dev)
-    off = None
-    if allowed is not None:
-        off = np.ascontiguousarray(allowed_off, dtype=np.int64)
-    rc = lib().rts_token_logprobs(
-        _ptr(logits), B, V, ld, _ptr(tokens), int(top_n),
-        _ptr(allowed), None if off is None else off.ctypes.data_as(ctypes.c_void_p),
-        _ptr(token_lp), _ptr(top_ids) if top_n > 0 else None,
-        _ptr(top_lp) if top_n > 0 else None, _ptr(ws), ws.numel(), _stream_handle(stream))
-    _check(rc)
-    return dict(token_lp=token_lp, top_ids=top_ids, top_lp=top_lp)
+    return LogprobCall(logits, tokens, top_n, allowed, allowed_off, workspace,
+                       stream)().results()
 
 
-__all__ = ["sample_tokens", "token_logprobs", "SampleCall", "workspace_bytes",
+__all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
            "make_workspace", "row_params", "RowParams", "RTSError", "lib"]

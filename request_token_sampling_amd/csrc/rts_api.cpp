@@ -115,6 +115,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       const int32_t *history_len,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
+                      uint64_t *counters, int64_t counter_stride,
                       void *workspace, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
@@ -190,6 +191,8 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.kept_ids = kept_ids ? kept_ids + rts::kMaxK * r0 : nullptr;
         a.kept_logits = kept_logits ? kept_logits + rts::kMaxK * r0 : nullptr;
         a.philox_x0 = philox_x0 ? philox_x0 + r0 : nullptr;
+        a.counters = counters ? counters + r0 : nullptr;
+        a.counter_stride = counter_stride;
         a.V = (int32_t)V;
         a.nchunks = (int32_t)chunks_for(V, ept);
         a.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);

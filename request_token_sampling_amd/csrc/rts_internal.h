@@ -56,6 +56,8 @@ struct SampleArgs {
     int32_t *kept_ids;
     float *kept_logits;
     uint32_t *philox_x0;
+    uint64_t *counters;     // device-resident counters (NULL: use row[].counter)
+    int64_t counter_stride; // added to counters[] by every call
     int32_t V;
     int32_t nchunks;
     int32_t keys_stride;   // keys per row slot in the workspace

@@ -12,7 +12,10 @@
 // the chunk lists into the kept sequence and one wavefront runs the cuts and
 // the draw: min_p (head + logf(min_p), computed in fp32), top_p over the
 // min_p survivors, temperature, and the Philox4x32-10 draw keyed by
-// (seed, counter) ("A persistent per-request draw counter" paragraph).
+// (seed, counter) ("A persistent per-request draw counter" paragraph).  The
+// counter may live in device memory, where the call advances it, so a
+// captured graph replaying the call keeps drawing fresh numbers ("Problem":
+// a captured sampler would otherwise repeat its draws).
 #include "rts_select.h"
 
 namespace rts {
@@ -127,6 +130,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     if (a.kept_logits) a.kept_logits[(int64_t)slot * kMaxK + lane] = y;
 
     const float y0 = lane_f32(y, 0);
+    // the row's Philox counter: device-resident when given (read here, then
+    // advanced below), else the caller's value from the argument block
+    const uint64_t ctr = a.counters ? a.counters[slot] : R.counter;
     int m = 1, n = 1, pick = 0;
     uint32_t x0 = 0u;
     if (!greedy) {
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         const bool head_masked = (y0 == -INFINITY);
         const double d = (lane < k && !head_masked) ? exp(dy) : 0.0;
         const double w = (lane < k && !head_masked) ? exp(dy / (double)R.temperature) : 0.0;
-        x0 = philox4x32_10_x0(R.counter, R.seed);
+        x0 = philox4x32_10_x0(ctr, R.seed);
         // min_p: keep the prefix with logit >= head + logf(min_p), in fp32.
         const float thr = y0 + R.lnp;
         m = __popcll(__ballot(lane < k && y >= thr));
@@ -172,6 +178,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
             a.counts[3 * (int64_t)slot + 2] = n;
         }
         if (a.philox_x0) a.philox_x0[slot] = x0;
+        if (a.counters) a.counters[slot] = ctr + (uint64_t)a.counter_stride;
         a.tickets[slot] = 0u;  // ready for the next launch on this workspace
     }
 }

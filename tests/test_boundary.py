@@ -54,7 +54,7 @@ def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws
     if hist_len is not None:
         hl = (ctypes.c_int32 * len(hist_len))(*hist_len)
     return L.rts_sample_tokens(logits, B, V, V if ld is None else ld, arr, history, H, ldh, hl,
-                               token, None, None, None, None, ws, ws_bytes, None)
+                               token, None, None, None, None, None, 0, ws, ws_bytes, None)
 
 
 SAMPLED = dict(temperature=0.7, top_k=20, top_p=0.9, min_p=0.05, seed=1, counter=0)

@@ -269,3 +269,60 @@ def test_workspace_reuse_across_calls():
     for a, b in outs[1:]:
         assert np.array_equal(a, outs[0][0]) and np.array_equal(b, outs[0][1])
     assert int(ws[:512].view(torch.int32).abs().sum().item()) == 0
+
+
+# ------------------------------------------------- device-resident counters
+def test_device_counters_advance_per_call():
+    """With device counters, call i draws with c0 + i*stride and the call
+    leaves c0 + (i+1)*stride behind (the caller's counter, in HBM)."""
+    w = W.tiny()
+    x, params = w["logits"], w["sampled"]
+    c0 = np.array([5, 9, 2**40 + 7, 0], np.int64)
+    ctr = to_dev(c0)
+    xd = to_dev(x)
+    stride = 3
+    for call in range(3):
+        say("case device counters call", call)
+        out = R.sample_tokens(xd, params, counters=ctr, counter_stride=stride)
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy() for k, v in out.items()}
+        want = [dict(p, counter=int(c0[r]) + call * stride) for r, p in enumerate(params)]
+        compare_sample(g, oracle_sample(x, want), f"device counters call {call}")
+    assert np.array_equal(ctr.cpu().numpy(), c0 + 3 * stride)
+
+
+def test_graph_replay_draws_fresh_numbers():
+    """A captured call replayed three times (eager work and a sync between
+    replays) draws with the advancing device counters every time."""
+    rng = np.random.default_rng(21)
+    Vx = 50000
+    x = rng.normal(0, 2, (3, Vx)).astype(np.float32)
+    params = [sampled(top_k=40, top_p=0.9, temperature=1.3, seed=77),
+              sampled(top_k=7, temperature=0.6, seed=78),
+              W.row_params()]
+    c0 = np.array([100, 200, 300], np.int64)
+    xd = to_dev(x)
+    ctr = to_dev(c0)
+    call = R.SampleCall(xd, params, counters=ctr, counter_stride=1)
+    call()                                     # eager warm-up: loads the kernel
+    torch.cuda.synchronize()
+    ctr.copy_(to_dev(c0))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    assert np.array_equal(ctr.cpu().numpy(), c0), "capture must not run the call"
+    seen = set()
+    for rep in range(3):
+        say("case graph replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy().copy() for k, v in call.results().items()}
+        want = [dict(p, counter=int(c0[r]) + rep) for r, p in enumerate(params)]
+        compare_sample(g, oracle_sample(x, want), f"graph replay {rep}")
+        seen.add(int(g["philox_x0"].view(np.uint32)[0]))
+        float((xd * 2.0).sum().item())         # eager work between replays
+        torch.cuda.synchronize()
+    assert len(seen) == 3, "every replay must draw a fresh number"
+    assert np.array_equal(ctr.cpu().numpy(), c0 + 3)
