@@ -255,8 +255,12 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (ws_bytes < need)
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
+    // Restricted rows take the gather-once kernel when their list is short
+    // enough and its LDS (bitmap + member list) fits, else the bitmap-walking
+    // kernel (bitmap only).
     const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
-    bool any_restricted = false;
+    const size_t fast_lds = bitmap_bytes + (size_t)rts::kAllowedFast * 4u;
+    bool any_restricted = false, fast_fits = false;
     if (allowed != nullptr) {
         if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");
         for (int64_t r = 0; r < B; ++r) {
@@ -265,9 +269,10 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
             if (allowed_off[r + 1] > allowed_off[r]) any_restricted = true;
         }
         if (any_restricted) {
-            const size_t lds = bitmap_bytes + rts::kAllowedStaticLds;
-            if (V > (1 << 19) || lds > max_lds_per_block())
+            const size_t max_lds = V > (1 << 19) ? 0 : max_lds_per_block();
+            if (bitmap_bytes + rts::kAllowedStaticLds > max_lds)
                 return fail(RTS_EINVAL, "allowed lists need V <= 2^19 (V = %lld)", (long long)V);
+            fast_fits = fast_lds + rts::kAllowedStaticLds <= max_lds;
         }
     }
 
@@ -291,31 +296,31 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     base.partials = reinterpret_cast<float2 *>(ws + rts::kTicketBytes +
                                                (size_t)rows_ws * rts::keys_bytes_per_row(V));
 
-    // Unrestricted rows through the full-row reducer, restricted rows through
-    // the gather kernel; each in launches of up to 64 rows.
-    for (int pass = 0; pass < 2; ++pass) {
-        const bool want_restricted = pass == 1;
-        if (want_restricted && !any_restricted) break;
+    // kind 0: unrestricted rows (full-row reducer); 1: short lists; 2: long lists.
+    // Each kind in launches of up to 64 rows.
+    for (int kind = 0; kind < 3; ++kind) {
+        if (kind > 0 && !any_restricted) break;
         rts::LogprobArgs a = base;
         int n = 0;
         auto flush = [&]() -> int {
             if (n == 0) return 0;
             a.rows = n;
             int e;
-            if (want_restricted) {
-                e = rts::launch_logprobs_allowed(a, bitmap_bytes, stream);
-            } else {
+            if (kind == 0) {
                 const int ept = choose_ept(n, V);
                 a.nchunks = (int32_t)chunks_for(V, ept);
-                const bool vec = is_vec_ok(logits, ld);
-                e = rts::launch_logprobs_full(a, ept, vec, stream);
+                e = rts::launch_logprobs_full(a, ept, is_vec_ok(logits, ld), stream);
+            } else {
+                e = rts::launch_logprobs_allowed(a, kind == 1 ? fast_lds : bitmap_bytes,
+                                                 kind == 2, stream);
             }
             n = 0;
             return e;
         };
         for (int64_t r = 0; r < B; ++r) {
             const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
-            if ((cnt > 0) != want_restricted) continue;
+            const int row_kind = cnt == 0 ? 0 : ((fast_fits && cnt <= rts::kAllowedFast) ? 1 : 2);
+            if (row_kind != kind) continue;
             rts::LogprobRow &lr = a.row[n++];
             lr.row = (int32_t)r;
             lr.allowed_off = allowed ? allowed_off[r] : 0;

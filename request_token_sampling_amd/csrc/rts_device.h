@@ -65,20 +65,6 @@ __device__ __forceinline__ uint64_t lanes_below_mask()
     return (1ull << lane_id()) - 1ull;
 }
 
-__device__ __forceinline__ float wave_max_f32(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
 // ---------------------------------------------------------------------------
 // DPP (data-parallel primitives) cross-lane steps.  Row ops move data inside
 // 16-lane rows; row_bcast15/31 carry a row's last lane into the next rows.
@@ -159,6 +145,41 @@ __device__ __forceinline__ double lane_f64(double v, int l)
 __device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l)
 {
     return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | lane_u32((uint32_t)v, l);
+}
+
+// Wave reductions built on the DPP steps; every lane gets the result.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ float dpp_max_f32(float v)
+{
+    // lanes without a source keep -inf, the identity of the maximum
+    const float o = __int_as_float(__builtin_amdgcn_update_dpp(
+        (int)0xFF800000, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, false));
+    return fmaxf(v, o);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v)
+{
+    v = dpp_max_f32<kRowShr1>(v);
+    v = dpp_max_f32<kRowShr2>(v);
+    v = dpp_max_f32<kRowShr4, 0xF, 0xE>(v);
+    v = dpp_max_f32<kRowShr8, 0xF, 0xC>(v);
+    v = dpp_max_f32<kRowBcast15, 0xA, 0xF>(v);
+    v = dpp_max_f32<kRowBcast31, 0xC, 0xF>(v);
+    return lane_f32(v, 63);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) { return lane_f64(wave_scan_f64(v), 63); }
+
+__device__ __forceinline__ float wave_sum_f32(float x)
+{
+    float s = x + __uint_as_float(dpp_u32<kRowShr1>(__float_as_uint(x)));
+    s = s + __uint_as_float(dpp_u32<kRowShr2>(__float_as_uint(x)));
+    s = s + __uint_as_float(dpp_u32<kRowShr3>(__float_as_uint(x)));
+    s = s + __uint_as_float(dpp_u32<kRowShr4, 0xF, 0xE>(__float_as_uint(s)));
+    s = s + __uint_as_float(dpp_u32<kRowShr8, 0xF, 0xC>(__float_as_uint(s)));
+    s = s + __uint_as_float(dpp_u32<kRowBcast15, 0xA, 0xF>(__float_as_uint(s)));
+    s = s + __uint_as_float(dpp_u32<kRowBcast31, 0xC, 0xF>(__float_as_uint(s)));
+    return lane_f32(s, 63);
 }
 
 // Largest t (to `bits` leading bits) with #{keys >= t} >= k, over the four

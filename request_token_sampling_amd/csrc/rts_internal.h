@@ -23,8 +23,13 @@ constexpr int kMinWavesPerSimd = 5;
 //   [512, ...)   per row slot: chunk candidate keys, then logprob partials
 constexpr size_t kTicketBytes = 512;
 
-// Static LDS of the allowed-ids kernel besides its vocabulary bitmap.
+// Static LDS of the allowed-ids kernels besides their dynamic bitmap / list.
 constexpr size_t kAllowedStaticLds = 10240;
+// Rows whose allowed list holds at most kAllowedFast ids gather their members
+// once into registers (kAllowedPerThread per thread); longer lists walk the
+// bitmap in every pass.
+constexpr int kAllowedPerThread = 16;
+constexpr int kAllowedFast = kAllowedPerThread * kBlock;
 
 inline int64_t max_chunks(int64_t V) { return (V + kMinChunk - 1) / kMinChunk; }
 inline size_t keys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxK * 8u; }
@@ -95,7 +100,7 @@ struct LogprobArgs {
 // Launchers (return a hipError_t as int).
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s);
-int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, hipStream_t s);
+int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s);
 int launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
 
 }  // namespace rts

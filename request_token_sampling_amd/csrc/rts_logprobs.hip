@@ -36,8 +36,7 @@ __device__ __forceinline__ float2 block_max_sum(SelectSmem &sm, float m, float s
     float c;
     if (M == -INFINITY) c = s;
     else c = (m == -INFINITY) ? 0.0f : s * __expf(m - M);
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
+    c = wave_sum_f32(c);
     if (lane == 0) red[4 + wave] = c;
     __syncthreads();
     const float S = (red[4] + red[5]) + (red[6] + red[7]);
@@ -120,7 +119,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
     double M = -INFINITY;
     for (int c = lane; c < a.nchunks; c += 64)
         M = fmax(M, (double)__uint_as_float((uint32_t)read_published_u64(P + c)));
-    for (int d = 32; d >= 1; d >>= 1) M = fmax(M, __shfl_xor(M, d, 64));
+    M = (double)wave_max_f32((float)M);  // the chunk maxima are floats
     double S = 0.0;
     for (int c = lane; c < a.nchunks; c += 64) {
         const uint64_t w = read_published_u64(P + c);
@@ -150,8 +149,10 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
 
 static_assert(sizeof(SelectSmem) + 4 <= kAllowedStaticLds, "static LDS bound");
 
-// One workgroup per restricted row.  Dynamic LDS: the vocabulary bitmap.
-__global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobArgs a)
+// One workgroup per restricted row whose list is longer than kAllowedFast:
+// the members are walked in the bitmap for each pass.  Dynamic LDS: the
+// vocabulary bitmap.
+__global__ __launch_bounds__(kBlock) void logprob_allowed_wide_kernel(const LogprobArgs a)
 {
     extern __shared__ uint32_t bm[];
     __shared__ SelectSmem sm;
@@ -209,8 +210,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
     s = wave_sum_f64(s);
     double *dred = reinterpret_cast<double *>(sm.cand);
     if (lane == 0) dred[tid >> 6] = s;
-    int nm = nmem;
-    for (int d = 32; d >= 1; d >>= 1) nm += __shfl_xor(nm, d, 64);
+    const int nm = (int)wave_sum_f64((double)nmem);
     if (lane == 0) sm.wave_cnt[tid >> 6] = (uint32_t)nm;
     __syncthreads();
     const double S = (dred[0] + dred[1]) + (dred[2] + dred[3]);
@@ -289,6 +289,165 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
     }
 }
 
+
+// Block-wide exclusive prefix of one count per thread (wave DPP scan, then the
+// wave totals through LDS); returns the thread's offset and the block total.
+__device__ __forceinline__ uint32_t block_excl_scan(SelectSmem &sm, uint32_t c, uint32_t *total)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const double incl = wave_scan_f64((double)c);   // exact for counts < 2^53
+    const uint32_t wincl = (uint32_t)incl;
+    if (lane == 63) sm.wave_cnt[wave] = wincl;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t t = sm.wave_cnt[w];
+        base += (w < wave) ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + wincl - c;
+}
+
+// One workgroup per restricted row with at most kAllowedFast listed ids.  The
+// named ids are marked in an LDS bitmap of the vocabulary (duplicates collapse,
+// foreign ids are ignored), the members are compacted in id-word order into an
+// LDS list, and their logits are gathered once, in one batch, into registers;
+// the max, the fp64 sum of exponentials and the top-K all run from there.
+// Dynamic LDS: the bitmap, then the member list.
+__global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobArgs a)
+{
+    extern __shared__ uint32_t bm[];
+    __shared__ SelectSmem sm;
+
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const LogprobRow R = a.row[blockIdx.x];
+    const int row = R.row;
+    const int V = a.V;
+    const int K = a.top_n;
+    const int nw = (V + 31) >> 5;
+    int32_t *list = reinterpret_cast<int32_t *>(bm + nw);
+    const float *x = a.logits + (int64_t)row * a.ld;
+
+    for (int w = tid; w < nw; w += kBlock) bm[w] = 0u;
+    __syncthreads();
+    const int32_t *ids = a.allowed + R.allowed_off;
+    for (int j = tid; j < (int)R.allowed_cnt; j += kBlock) {
+        const int32_t id = ids[j];
+        if (id >= 0 && id < V) atomicOr(&bm[id >> 5], 1u << (id & 31));
+    }
+    __syncthreads();
+
+    // members of the thread's words, compacted in a fixed order
+    uint32_t mine = 0;
+    for (int w = tid; w < nw; w += kBlock) mine += (uint32_t)__popc(bm[w]);
+    uint32_t members = 0;
+    uint32_t pos = block_excl_scan(sm, mine, &members);
+    for (int w = tid; w < nw; w += kBlock) {
+        uint32_t bits = bm[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            list[pos++] = (w << 5) + b;
+        }
+    }
+    __syncthreads();
+
+    // one batch of gathers: member f = tid + 256 * j
+    float v[kAllowedPerThread];
+#pragma unroll
+    for (int j = 0; j < kAllowedPerThread; ++j) {
+        const uint32_t f = (uint32_t)(tid + j * kBlock);
+        v[j] = (f < members) ? sanitize(x[list[f]]) : __builtin_nanf("");
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kAllowedPerThread; ++j) lmax = (v[j] == v[j]) ? fmaxf(lmax, v[j]) : lmax;
+    float *red = reinterpret_cast<float *>(sm.red);
+    const float wm = wave_max_f32(lmax);
+    if (lane == 0) red[wave] = wm;
+    __syncthreads();
+    const float Mf = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const double M = (double)Mf;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < kAllowedPerThread; ++j)
+        if (v[j] == v[j]) s += (Mf == -INFINITY) ? 1.0 : exp((double)v[j] - M);
+    s = wave_sum_f64(s);
+    double *dred = reinterpret_cast<double *>(sm.cand);
+    if (lane == 0) dred[wave] = s;
+    __syncthreads();
+    const double S = (dred[0] + dred[1]) + (dred[2] + dred[3]);
+    __syncthreads();
+    const bool empty = members == 0u;
+    const bool uniform = !empty && Mf == -INFINITY;
+    const double L = empty ? INFINITY : (uniform ? log(S) : M + log(S));
+
+    if (K > 0) {
+        // top-K of the members: lane maxima -> threshold -> compaction -> rank
+        sm.lane_keys[tid] = ((uint32_t)tid < members) ? value_key(lmax) : 0u;
+        __syncthreads();
+        const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
+                                sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
+        const float tf = key_threshold(kth_largest_key_256<16>(lk, K));
+        const uint64_t below = lanes_below_mask();
+        uint64_t *wc = sm.cand + wave * kCap;
+        uint32_t wcnt = 0;
+#pragma unroll
+        for (int j = 0; j < kAllowedPerThread; ++j) {
+            const uint32_t f = (uint32_t)(tid + j * kBlock);
+            const bool c = v[j] >= tf;               // NaN (no member) never passes
+            const uint64_t m = __ballot(c);
+            if (m) {
+                const uint32_t p = wcnt + (uint32_t)__popcll(m & below);
+                if (c && p < (uint32_t)kCap) wc[p] = cand_key(v[j], (uint32_t)list[f]);
+                wcnt += (uint32_t)__popcll(m);
+            }
+        }
+        if (lane == 0) sm.wave_cnt[wave] = wcnt;
+        pad_region(sm, wave, wcnt);
+        __syncthreads();
+        if (!any_overflow(sm)) {
+            rank_candidates(sm, K, ToLds{sm.sel});
+        } else {
+            // massive ties at the threshold: K argmax rounds over the members
+            uint64_t prev = ~0ull;
+            for (int r = 0; r < K; ++r) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int j = 0; j < kAllowedPerThread; ++j) {
+                    const uint32_t f = (uint32_t)(tid + j * kBlock);
+                    if (f < members) {
+                        const uint64_t key = cand_key(v[j], (uint32_t)list[f]);
+                        best = (key < prev && key > best) ? key : best;
+                    }
+                }
+                best = block_max_u64(sm, best);
+                if (tid == 0) sm.sel[r] = best;
+                prev = best;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (tid == 0) {
+        const int32_t t = a.tokens[row];
+        float lp = -INFINITY;
+        if (t >= 0 && t < V && ((bm[t >> 5] >> (t & 31)) & 1u))
+            lp = uniform ? (float)(-L) : (float)((double)sanitize(x[t]) - L);
+        a.token_lp[row] = lp;
+    }
+    if (tid < K) {
+        const uint64_t key = sm.sel[tid];
+        const bool valid = key != 0ull;
+        a.top_ids[(int64_t)row * K + tid] = valid ? (int32_t)key_index(key) : -1;
+        a.top_lp[(int64_t)row * K + tid] =
+            valid ? (uniform ? (float)(-L) : (float)((double)key_logit(key) - L)) : -INFINITY;
+    }
+}
+
 template <int EPT, bool VEC>
 static int launch_full_t(const LogprobArgs &a, hipStream_t s)
 {
@@ -308,10 +467,14 @@ int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s)
     }
 }
 
-int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, hipStream_t s)
+int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s)
 {
-    hipLaunchKernelGGL(logprob_allowed_kernel, dim3((unsigned)a.rows), dim3(kBlock),
-                       (unsigned)lds_bytes, s, a);
+    if (wide)
+        hipLaunchKernelGGL(logprob_allowed_wide_kernel, dim3((unsigned)a.rows), dim3(kBlock),
+                           (unsigned)lds_bytes, s, a);
+    else
+        hipLaunchKernelGGL(logprob_allowed_kernel, dim3((unsigned)a.rows), dim3(kBlock),
+                           (unsigned)lds_bytes, s, a);
     return (int)hipGetLastError();
 }
 
