@@ -68,6 +68,27 @@ typedef struct rts_row_params {
     uint64_t counter;      /* Philox counter (low word, high word, 0, 0); caller-owned       */
 } rts_row_params;
 
+/*
+ * Raw-logit logprobs computed in the same pass over the logits as the draw
+ * (#3200, "Approach": the reported distribution is the model's own, taken
+ * before penalties and temperature).  Given to rts_sample_tokens, it asks for
+ * what rts_token_logprobs would report, unrestricted, for the tokens that
+ * call samples, without reading the logits a second time.
+ *   top_n     0..20 entries of top_ids / top_lp per row.
+ *   reserved  must be 0.
+ *   token_lp  device f32 [B]: logprob of the sampled token.
+ *   top_ids   device int32 [B][top_n]; top_lp device f32 [B][top_n]: the
+ *             row's largest raw logits in (logit desc, index asc) order and
+ *             their logprobs.  Both may be NULL when top_n = 0.
+ */
+typedef struct rts_logprob_request {
+    int32_t top_n;
+    int32_t reserved;
+    float *token_lp;
+    int32_t *top_ids;
+    float *top_lp;
+} rts_logprob_request;
+
 /* Bytes of workspace that calls with up to B rows of V logits need
  * (both entry points).  *bytes is set on RTS_OK. */
 int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes);
@@ -102,11 +123,13 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
  *               numbers on every replay instead of repeating them (page
  *               "#19 ...", "Problem": a captured sampler would replay the same
  *               draws forever; "A persistent per-request draw counter").
+ *   lp          host, or NULL for no logprobs: see rts_logprob_request.
  * Errors: RTS_EINVAL for B < 0, V out of range, ld < V, NULL logits/token,
  * a row with NaN or infinite temperature, top_k outside 1..64 on a sampled
  * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
  * non-finite penalties, history_row >= H or set without history, a window
- * longer than RTS_MAX_WINDOW, or reserved != 0; RTS_ENOSPC for a short
+ * longer than RTS_MAX_WINDOW, reserved != 0, or an lp request with top_n
+ * outside 0..20, reserved != 0 or a NULL output it needs; RTS_ENOSPC for a short
  * workspace; RTS_EDEVICE if a launch fails.  B = 0 is a no-op.
  */
 int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
@@ -116,6 +139,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
                       uint64_t *counters, int64_t counter_stride,
+                      const rts_logprob_request *lp,
                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -128,7 +152,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
  *               allowed_off[r+1]); NULL for no restriction.  A row with an
  *               empty range is unrestricted; duplicates count once; ids
  *               outside [0, V) are ignored.  Restricted rows need V <= 2^19.
- *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] = 0.
+ *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] >= 0.
  * Outputs (device): token_lp f32 [B] (-inf when the token is outside the
  * row's domain), top_ids int32 [B][top_n] and top_lp f32 [B][top_n], the
  * domain's largest logits in (logit desc, index asc) order, padded with

@@ -50,6 +50,21 @@ class RowParams(ctypes.Structure):
 
 assert ctypes.sizeof(RowParams) == 56
 
+
+class LogprobRequest(ctypes.Structure):
+    """Mirror of rts_logprob_request: raw-logit logprobs of the sampled tokens
+    computed in the sampling call's own pass over the logits."""
+    _fields_ = [
+        ("top_n", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("token_lp", ctypes.c_void_p),
+        ("top_ids", ctypes.c_void_p),
+        ("top_lp", ctypes.c_void_p),
+    ]
+
+
+assert ctypes.sizeof(LogprobRequest) == 32
+
 _DEFAULTS = dict(temperature=0.0, top_k=0, top_p=1.0, min_p=0.0, penalty_repeat=1.0,
                  penalty_freq=0.0, penalty_present=0.0, penalty_last_n=0, history_row=-1,
                  reserved=0, seed=0, counter=0)
@@ -69,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L.rts_workspace_bytes.argtypes = [I64, I64, ctypes.POINTER(ctypes.c_size_t)]
         L.rts_workspace_init.argtypes = [P, SZ, P]
         L.rts_sample_tokens.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P, P, P,
-                                        I64, P, SZ, P]
+                                        I64, P, P, SZ, P]
         L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
                   "rts_token_logprobs"):
@@ -137,7 +152,7 @@ class SampleCall:
     with ``set_params``."""
 
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
-                 stream=None, counters=None, counter_stride=0):
+                 stream=None, counters=None, counter_stride=0, logprobs=None):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -159,6 +174,16 @@ class SampleCall:
                 raise ValueError("counters must be a CUDA int64 tensor with one entry per row")
         self.counters = counters
         self.counter_stride = int(counter_stride)
+        # logprobs=top_n (0..20): raw-logit logprobs of the sampled tokens in the same pass
+        self.lp = None
+        if logprobs is not None:
+            n = int(logprobs)
+            self.token_lp = torch.empty(self.B, dtype=torch.float32, device=dev)
+            self.top_ids = torch.empty((self.B, max(n, 0)), dtype=torch.int32, device=dev)
+            self.top_lp = torch.empty((self.B, max(n, 0)), dtype=torch.float32, device=dev)
+            self.lp = LogprobRequest(n, 0, self.token_lp.data_ptr(),
+                                     self.top_ids.data_ptr() if n > 0 else None,
+                                     self.top_lp.data_ptr() if n > 0 else None)
         self.set_params(params)
         self.stream = stream
 
@@ -173,6 +198,7 @@ class SampleCall:
             None if self.hist_len is None else self.hist_len.ctypes.data_as(ctypes.c_void_p),
             _ptr(self.token), _ptr(self.counts), _ptr(self.kept_ids), _ptr(self.kept_logits),
             _ptr(self.philox_x0), _ptr(self.counters), self.counter_stride,
+            None if self.lp is None else ctypes.byref(self.lp),
             _ptr(self.workspace), self.workspace.numel(), None]
 
     def __call__(self):
@@ -180,27 +206,33 @@ class SampleCall:
             self._build_args()
         a = self._args
         a[0] = self.logits.data_ptr()
-        a[18] = _stream_handle(self.stream)
+        a[19] = _stream_handle(self.stream)
         _check(lib().rts_sample_tokens(*a))
         return self
 
     def results(self) -> dict:
         """Device tensors; philox_x0 holds the uint32 words' bits as int32."""
-        return dict(token=self.token, counts=self.counts, kept_ids=self.kept_ids,
-                    kept_logits=self.kept_logits, philox_x0=self.philox_x0)
+        r = dict(token=self.token, counts=self.counts, kept_ids=self.kept_ids,
+                 kept_logits=self.kept_logits, philox_x0=self.philox_x0)
+        if self.lp is not None:
+            r.update(token_lp=self.token_lp, top_ids=self.top_ids, top_lp=self.top_lp)
+        return r
 
 
 def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
-                  stream=None, counters=None, counter_stride=0) -> dict:
+                  stream=None, counters=None, counter_stride=0, logprobs=None) -> dict:
     """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
 
     params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
     history: CUDA int32 [H][ldh] with host lengths history_len[H], or None.
     Returns device tensors token[B], counts[B][3], kept_ids[B][64],
     kept_logits[B][64], philox_x0[B].  counters: optional CUDA int64 [B]
-    device-resident Philox counters, advanced by counter_stride per call."""
+    device-resident Philox counters, advanced by counter_stride per call.
+    logprobs: None, or top_n in 0..20 to add token_lp[B], top_ids[B][top_n]
+    and top_lp[B][top_n], the raw-logit logprobs of the sampled tokens,
+    computed in the same pass over the logits."""
     return SampleCall(logits, params, history, history_len, workspace, stream, counters,
-                      counter_stride)().results()
+                      counter_stride, logprobs)().results()
 
 
 class LogprobCall:
@@ -253,4 +285,4 @@ def token_logprobs(logits, tokens, top_n: int, allowed=None, allowed_off=None,
 
 
 __all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
-           "make_workspace", "row_params", "RowParams", "RTSError", "lib"]
+           "make_workspace", "row_params", "RowParams", "LogprobRequest", "RTSError", "lib"]

@@ -91,10 +91,7 @@ int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes)
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
     if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
     const int64_t rows = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
-    const size_t per_row = rts::keys_bytes_per_row(V) + rts::partial_bytes_per_row(V);
-    size_t total = rts::kTicketBytes + (size_t)(rows > 0 ? rows : 1) * per_row;
-    total = (total + 255u) & ~(size_t)255u;
-    *bytes = total;
+    *bytes = rts::ws_layout(rows, V).total;
     return RTS_OK;
 }
 
@@ -116,6 +113,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
                       uint64_t *counters, int64_t counter_stride,
+                      const rts_logprob_request *lp,
                       void *workspace, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
@@ -129,6 +127,14 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (token == nullptr) return fail(RTS_EINVAL, "token is NULL");
     if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
     if (H < 0 || ldh < 0) return fail(RTS_EINVAL, "H = %lld, ldh = %lld", (long long)H, (long long)ldh);
+    if (lp != nullptr) {
+        if (lp->top_n < 0 || lp->top_n > RTS_MAX_TOP_N)
+            return fail(RTS_EINVAL, "lp->top_n = %d outside 0..20", lp->top_n);
+        if (lp->reserved != 0) return fail(RTS_EINVAL, "lp->reserved is not 0");
+        if (lp->token_lp == nullptr) return fail(RTS_EINVAL, "lp->token_lp is NULL");
+        if (lp->top_n > 0 && (lp->top_ids == nullptr || lp->top_lp == nullptr))
+            return fail(RTS_EINVAL, "lp->top_ids / lp->top_lp are NULL with top_n = %d", lp->top_n);
+    }
     size_t need = 0;
     rts_workspace_bytes(B, V, &need);
     if (ws_bytes < need)
@@ -176,6 +182,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     }
 
     char *ws = static_cast<char *>(workspace);
+    const rts::WsLayout L = rts::ws_layout(B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch, V);
     for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
         const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
         const int ept = choose_ept(rows, V);
@@ -184,7 +191,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.logits = logits + r0 * ld;
         a.ld = ld;
         a.history = history;
-        a.keys = reinterpret_cast<uint64_t *>(ws + rts::kTicketBytes);
+        a.keys = reinterpret_cast<uint64_t *>(ws + L.keys);
         a.tickets = reinterpret_cast<uint32_t *>(ws);
         a.token = token + r0;
         a.counts = counts ? counts + 3 * r0 : nullptr;
@@ -197,6 +204,18 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.nchunks = (int32_t)chunks_for(V, ept);
         a.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
         a.rows = rows;
+        a.early_xcds = rows * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
+        if (lp != nullptr) {
+            a.lp_on = 1;
+            a.lp_topn = lp->top_n;
+            a.raw_keys = reinterpret_cast<uint64_t *>(ws + L.raw);
+            a.raw_stride = (int32_t)(rts::rawkeys_bytes_per_row(V) / 8u);
+            a.partials = reinterpret_cast<uint64_t *>(ws + L.partials);
+            a.partial_stride = (int32_t)rts::max_chunks(V);
+            a.lp_token = lp->token_lp + r0;
+            a.lp_ids = lp->top_n > 0 ? lp->top_ids + r0 * lp->top_n : nullptr;
+            a.lp_top = lp->top_n > 0 ? lp->top_lp + r0 * lp->top_n : nullptr;
+        }
         for (int i = 0; i < rows; ++i) {
             const rts_row_params &p = params[r0 + i];
             rts::SampleRow &s = a.row[i];
@@ -283,7 +302,9 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     base.ld = ld;
     base.tokens = tokens;
     base.allowed = allowed;
-    base.keys = reinterpret_cast<uint64_t *>(ws + rts::kTicketBytes);
+    const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
+    const rts::WsLayout L = rts::ws_layout(rows_ws, V);
+    base.keys = reinterpret_cast<uint64_t *>(ws + L.keys);
     base.tickets = reinterpret_cast<uint32_t *>(ws + 256);
     base.token_lp = token_lp;
     base.top_ids = top_ids;
@@ -292,9 +313,7 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     base.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
     base.partial_stride = (int32_t)rts::max_chunks(V);
     base.top_n = top_n;
-    const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
-    base.partials = reinterpret_cast<float2 *>(ws + rts::kTicketBytes +
-                                               (size_t)rows_ws * rts::keys_bytes_per_row(V));
+    base.partials = reinterpret_cast<float2 *>(ws + L.partials);
 
     // kind 0: unrestricted rows (full-row reducer); 1: short lists; 2: long lists.
     // Each kind in launches of up to 64 rows.
@@ -309,6 +328,7 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
             if (kind == 0) {
                 const int ept = choose_ept(n, V);
                 a.nchunks = (int32_t)chunks_for(V, ept);
+                a.early_xcds = n * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
                 e = rts::launch_logprobs_full(a, ept, is_vec_ok(logits, ld), stream);
             } else {
                 e = rts::launch_logprobs_allowed(a, kind == 1 ? fast_lds : bitmap_bytes,

@@ -20,7 +20,8 @@ constexpr int kMinWavesPerSimd = 5;
 // Workspace layout (bytes from its start):
 //   [0, 256)     sampling tickets, one uint32 per row slot of a launch
 //   [256, 512)   logprob tickets
-//   [512, ...)   per row slot: chunk candidate keys, then logprob partials
+//   then, for every row slot of a launch: chunk candidate keys (64 per chunk),
+//   raw-logit top-K keys (20 per chunk) and (max, sum) partials (one per chunk)
 constexpr size_t kTicketBytes = 512;
 
 // Static LDS of the allowed-ids kernels besides their dynamic bitmap / list.
@@ -34,6 +35,22 @@ constexpr int kAllowedFast = kAllowedPerThread * kBlock;
 inline int64_t max_chunks(int64_t V) { return (V + kMinChunk - 1) / kMinChunk; }
 inline size_t keys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxK * 8u; }
 inline size_t partial_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * 8u; }
+inline size_t rawkeys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxTopN * 8u; }
+
+struct WsLayout {
+    size_t keys, raw, partials, total;
+};
+
+inline WsLayout ws_layout(int64_t rows_ws, int64_t V)
+{
+    WsLayout l;
+    const size_t r = (size_t)(rows_ws > 0 ? rows_ws : 1);
+    l.keys = kTicketBytes;
+    l.raw = l.keys + r * keys_bytes_per_row(V);
+    l.partials = l.raw + r * rawkeys_bytes_per_row(V);
+    l.total = (l.partials + r * partial_bytes_per_row(V) + 255u) & ~(size_t)255u;
+    return l;
+}
 
 // Per-row sampling parameters after host-side checking (56 bytes).
 struct SampleRow {
@@ -67,8 +84,22 @@ struct SampleArgs {
     int32_t nchunks;
     int32_t keys_stride;   // keys per row slot in the workspace
     int32_t rows;
+    int32_t early_xcds;    // 1: work only on blockIdx % 8 < 2 (see logical_block)
+    int32_t lp_topn;       // raw-logit logprobs in the same pass: top entries (0..20)
+    int32_t lp_on;         // 1: compute the raw logprobs of the sampled token
+    int32_t raw_stride;    // raw top-K keys per row slot in the workspace
+    int32_t partial_stride;
+    int32_t pad2_;
+    uint64_t *raw_keys;    // workspace: per row slot nchunks * lp_topn keys
+    uint64_t *partials;    // workspace: per row slot nchunks (max, sum) pairs
+    float *lp_token;       // outputs, row 0 of this launch
+    int32_t *lp_ids;
+    float *lp_top;
     SampleRow row[kRowsPerLaunch];
 };
+// HIP passes at most 4 KiB of kernel arguments.
+static_assert(sizeof(SampleArgs) <= 4096, "kernel argument block");
+
 
 struct LogprobRow {
     int64_t allowed_off;   // first id of the row's list in `allowed`
@@ -94,8 +125,16 @@ struct LogprobArgs {
     int32_t partial_stride;
     int32_t top_n;
     int32_t rows;
+    int32_t early_xcds;
+    int32_t pad_;
     LogprobRow row[kRowsPerLaunch];
 };
+
+// Launches with at most this many workgroups of work run on XCDs 0-1 only.
+constexpr int kEarlyXcdWork = 64;
+
+// Grid for `work` workgroups, padded for early-XCD placement when it applies.
+inline unsigned grid_for(int work, int early) { return early ? (unsigned)(((work + 1) / 2) * 8) : (unsigned)work; }
 
 // Launchers (return a hipError_t as int).
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);

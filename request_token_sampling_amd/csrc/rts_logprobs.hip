@@ -22,28 +22,6 @@ namespace rts {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Per-lane (max, sum) -> block (max, sum).  A lane whose values are all -inf
-// carries its element count as the sum (the uniform reading for an all -inf
-// domain); an empty lane carries (-inf, 0).
-__device__ __forceinline__ float2 block_max_sum(SelectSmem &sm, float m, float s)
-{
-    float *red = reinterpret_cast<float *>(sm.red);  // 8 floats
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const float wm = wave_max_f32(m);
-    if (lane == 0) red[wave] = wm;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float c;
-    if (M == -INFINITY) c = s;
-    else c = (m == -INFINITY) ? 0.0f : s * __expf(m - M);
-    c = wave_sum_f32(c);
-    if (lane == 0) red[4 + wave] = c;
-    __syncthreads();
-    const float S = (red[4] + red[5]) + (red[6] + red[7]);
-    __syncthreads();
-    return make_float2(M, S);
-}
-
 template <int EPT, bool VEC>
 __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const LogprobArgs a)
 {
@@ -52,8 +30,10 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
     __shared__ SelectSmem sm;
 
     const int tid = threadIdx.x;
-    const int slot = blockIdx.x / a.nchunks;
-    const int chunk = blockIdx.x - slot * a.nchunks;
+    const int lb = logical_block(a.early_xcds);
+    if (lb < 0 || lb >= a.rows * a.nchunks) return;  // padding workgroup
+    const int slot = lb / a.nchunks;
+    const int chunk = lb - slot * a.nchunks;
     const int row = a.row[slot].row;
     const int V = a.V;
     const int K = a.top_n;
@@ -98,9 +78,8 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
     }
     const float2 ms = block_max_sum(sm, lmax, lsum);
     if (tid == 0)
-        publish_u64(reinterpret_cast<uint64_t *>(a.partials) + (int64_t)slot * a.partial_stride +
-                        chunk,
-                    ((uint64_t)__float_as_uint(ms.y) << 32) | __float_as_uint(ms.x));
+        publish_partial(reinterpret_cast<uint64_t *>(a.partials) + (int64_t)slot * a.partial_stride +
+                            chunk, ms);
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
     if (K > 0) chunk_topk<EPT>(sm, v, base, V, K, list + (int64_t)chunk * K);
@@ -112,24 +91,11 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
 
     if ((tid >> 6) != 0) return;
     const int lane = lane_id();
-    // fp64 combination of the chunk pairs, each lane taking chunks
-    // lane, lane + 64, ... in order, then a fixed-shape wave reduction.
-    const uint64_t *P = reinterpret_cast<const uint64_t *>(a.partials) +
-                        (int64_t)slot * a.partial_stride;
-    double M = -INFINITY;
-    for (int c = lane; c < a.nchunks; c += 64)
-        M = fmax(M, (double)__uint_as_float((uint32_t)read_published_u64(P + c)));
-    M = (double)wave_max_f32((float)M);  // the chunk maxima are floats
-    double S = 0.0;
-    for (int c = lane; c < a.nchunks; c += 64) {
-        const uint64_t w = read_published_u64(P + c);
-        const float px = __uint_as_float((uint32_t)w), py = __uint_as_float((uint32_t)(w >> 32));
-        if (M == -INFINITY) S += (double)py;
-        else if (px != -INFINITY) S += (double)py * exp((double)px - M);
-    }
-    S = wave_sum_f64(S);
-    const bool uniform = (M == -INFINITY);
-    const double L = uniform ? log(S) : M + log(S);
+    double L;
+    bool uniform;
+    combine_partials(reinterpret_cast<const uint64_t *>(a.partials) +
+                         (int64_t)slot * a.partial_stride,
+                     a.nchunks, &L, &uniform);
 
     if (lane == 0) {
         const int32_t t = a.tokens[row];
@@ -407,10 +373,10 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
             }
         }
         if (lane == 0) sm.wave_cnt[wave] = wcnt;
-        pad_region(sm, wave, wcnt);
+        pad_region(own_cands(sm), wave, wcnt);
         __syncthreads();
-        if (!any_overflow(sm)) {
-            rank_candidates(sm, K, ToLds{sm.sel});
+        if (!any_overflow(own_cands(sm))) {
+            rank_candidates(sm, own_cands(sm), K, ToLds{sm.sel});
         } else {
             // massive ties at the threshold: K argmax rounds over the members
             uint64_t prev = ~0ull;
@@ -451,7 +417,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
 template <int EPT, bool VEC>
 static int launch_full_t(const LogprobArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((logprob_kernel<EPT, VEC>), dim3((unsigned)(a.rows * a.nchunks)),
+    hipLaunchKernelGGL((logprob_kernel<EPT, VEC>), dim3(grid_for(a.rows * a.nchunks, a.early_xcds)),
                        dim3(kBlock), 0, s, a);
     return (int)hipGetLastError();
 }

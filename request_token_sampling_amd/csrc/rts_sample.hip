@@ -20,11 +20,13 @@
 
 namespace rts {
 
-template <int EPT>
+template <int EPT, bool LP>
 struct SampleSmem {
     SelectSmem s;
     uint32_t pen_bits[EPT * kBlock / 32];  // one bit per id of the chunk
     uint32_t pen_cnt[EPT * kBlock / 2];    // two 16-bit counts per word
+    uint64_t raw_keys[LP ? 4 * kCap : 1];  // candidates of the raw top-K
+    uint32_t raw_cnt[4];
 };
 
 // llama.cpp-style penalty of an id seen c > 0 times in the window: the repeat
@@ -43,29 +45,14 @@ __device__ __forceinline__ float penalize(float v, uint32_t c, float rep, float 
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The chunk at `base` into registers, element e of the thread at
+// elem_index(base, e); ids past V (only in the last chunk) read as NaN.
 template <int EPT, bool VEC>
-__global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const SampleArgs a)
+__device__ __forceinline__ void load_chunk(const float *x, int base, int V, float (&v)[EPT])
 {
-    constexpr int CH = EPT * kBlock;
-    constexpr int NQ = EPT / 4;
-    __shared__ SampleSmem<EPT> sm;
-
     const int tid = threadIdx.x;
-    const int slot = blockIdx.x / a.nchunks;
-    const int chunk = blockIdx.x - slot * a.nchunks;
-    const SampleRow R = a.row[slot];
-    const int V = a.V;
-    const int n_eff = (int)(R.pack & 0xFFFFu);
-    const int k = (int)((R.pack >> 16) & 0x7Fu);
-    const bool greedy = ((R.pack >> 24) & 1u) != 0u;
-    const int base = chunk * CH;
-    const float *x = a.logits + (int64_t)slot * a.ld;
-
-    // Issue every load of the chunk first; the bitmap build below overlaps
-    // them.  Ids past V (only in the last chunk) read as NaN: never selected.
-    float v[EPT];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = 0; q < EPT / 4; ++q) {
         const int i0 = base + q * 1024 + tid * 4;
         if (VEC && i0 + 4 <= V) {
             const f32x4 t = *reinterpret_cast<const f32x4 *>(x + i0);
@@ -79,50 +66,15 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
                 v[4 * q + s] = (i0 + s < V) ? x[i0 + s] : __builtin_nanf("");
         }
     }
+}
 
-    if (n_eff > 0) {
-        for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
-        for (int w = tid; w < CH / 2; w += kBlock) sm.pen_cnt[w] = 0u;
-        __syncthreads();
-        const int32_t *h = a.history + R.hist_off;
-        for (int j = tid; j < n_eff; j += kBlock) {
-            const int32_t id = h[j];
-            const int rel = id - base;
-            if (id >= 0 && id < V && rel >= 0 && rel < CH) {
-                atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
-                atomicAdd(&sm.pen_cnt[rel >> 1], 1u << ((rel & 1) * 16));
-            }
-        }
-        __syncthreads();
-        // Only flagged ids look up a count; they leave sanitised.
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int rel = q * 1024 + tid * 4;
-            const uint32_t nib = (sm.pen_bits[rel >> 5] >> (rel & 31)) & 0xFu;
-            if (nib) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if ((nib >> s) & 1u) {
-                        const int r = rel + s;
-                        const uint32_t c = (sm.pen_cnt[r >> 1] >> ((r & 1) * 16)) & 0xFFFFu;
-                        v[4 * q + s] = penalize(sanitize(v[4 * q + s]), c, R.rep, R.freq, R.present);
-                    }
-                }
-            }
-        }
-    }
-
-    uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k);
-
-    if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.s.flag)) return;
-
-    // ---- the last workgroup of the row: merge, then the cuts and the draw.
-    list_topk(sm.s, list, a.nchunks, k);
-
-    if ((tid >> 6) != 0) return;
+// The cuts and the draw, run by wave 0 of the row's last workgroup on the
+// merged kept sequence sm.sel[0..k).  Leaves the sampled token in sm.flag.
+__device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
+                                         int slot, int k, bool greedy)
+{
     const int lane = lane_id();
-    const uint64_t key = (lane < k) ? sm.s.sel[lane] : 0ull;
+    const uint64_t key = (lane < k) ? sm.sel[lane] : 0ull;
     const bool valid = key != 0ull;
     const int32_t id = valid ? (int32_t)key_index(key) : -1;
     const float y = valid ? key_logit(key) : -INFINITY;
@@ -171,6 +123,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     }
     const int32_t tok = lane_i32(id, pick);
     if (lane == 0) {
+        sm.flag = (uint32_t)tok;
         a.token[slot] = tok;
         if (a.counts) {
             a.counts[3 * (int64_t)slot + 0] = k;
@@ -183,21 +136,150 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     }
 }
 
-template <int EPT, bool VEC>
+template <int EPT, bool VEC, bool LP>
+__global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const SampleArgs a)
+{
+    constexpr int CH = EPT * kBlock;
+    constexpr int NQ = EPT / 4;
+    __shared__ SampleSmem<EPT, LP> sm;
+
+    const int tid = threadIdx.x;
+    const int lb = logical_block(a.early_xcds);
+    if (lb < 0 || lb >= a.rows * a.nchunks) return;  // padding workgroup
+    const int slot = lb / a.nchunks;
+    const int chunk = lb - slot * a.nchunks;
+    const SampleRow R = a.row[slot];
+    const int V = a.V;
+    const int n_eff = (int)(R.pack & 0xFFFFu);
+    const int k = (int)((R.pack >> 16) & 0x7Fu);
+    const bool greedy = ((R.pack >> 24) & 1u) != 0u;
+    const int base = chunk * CH;
+    const float *x = a.logits + (int64_t)slot * a.ld;
+
+    // Issue every load of the chunk first; the bitmap build below overlaps
+    // them.  Ids past V read as NaN: never selected.
+    float v[EPT];
+    load_chunk<EPT, VEC>(x, base, V, v);
+
+    // Raw-logit logprobs in the same pass (page "#3200 ...", "Approach": the
+    // reported distribution is taken before penalties and temperature): the
+    // chunk's (max, sum) of the raw values, and their top-K unless the kept
+    // list will already be the raw top-K (no penalties and k_eff >= K).  The
+    // raw selection's candidates are compacted now, from the raw values, and
+    // ranked after the penalised selection, so only one set of values is
+    // held in registers at a time.
+    const int K = LP ? a.lp_topn : 0;
+    const bool raw_sel = LP && K > 0 && !(n_eff == 0 && k >= K);
+    const Cands rawc{sm.raw_keys, sm.raw_cnt};
+    uint64_t *raw_out = LP ? a.raw_keys + (int64_t)slot * a.raw_stride + (int64_t)chunk * K : nullptr;
+    bool raw_done = false;
+    if (LP) {
+        const float2 lms = lane_max_sum<EPT>(v, [&]() {
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) c += ((int)elem_index<EPT>(base, e) < V) ? 1 : 0;
+            return c;
+        });
+        const float2 ms = block_max_sum(sm.s, lms.x, lms.y);
+        if (tid == 0)
+            publish_partial(a.partials + (int64_t)slot * a.partial_stride + chunk, ms);
+        if (raw_sel) raw_done = chunk_compact<EPT>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
+    }
+
+    if (n_eff > 0) {
+        for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
+        for (int w = tid; w < CH / 2; w += kBlock) sm.pen_cnt[w] = 0u;
+        __syncthreads();
+        const int32_t *h = a.history + R.hist_off;
+        for (int j = tid; j < n_eff; j += kBlock) {
+            const int32_t id = h[j];
+            const int rel = id - base;
+            if (id >= 0 && id < V && rel >= 0 && rel < CH) {
+                atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
+                atomicAdd(&sm.pen_cnt[rel >> 1], 1u << ((rel & 1) * 16));
+            }
+        }
+        __syncthreads();
+        // Only flagged ids look up a count; they leave sanitised.
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rel = q * 1024 + tid * 4;
+            const uint32_t nib = (sm.pen_bits[rel >> 5] >> (rel & 31)) & 0xFu;
+            if (nib) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    if ((nib >> s) & 1u) {
+                        const int r = rel + s;
+                        const uint32_t c = (sm.pen_cnt[r >> 1] >> ((r & 1) * 16)) & 0xFFFFu;
+                        v[4 * q + s] = penalize(sanitize(v[4 * q + s]), c, R.rep, R.freq, R.present);
+                    }
+                }
+            }
+        }
+    }
+
+    uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
+    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k);
+
+    if (raw_sel && !raw_done) {
+        __syncthreads();  // the penalised selection's rank may still read sm.part
+        if (any_overflow(rawc)) load_chunk<EPT, VEC>(x, base, V, v);  // raw values again
+        chunk_finish<EPT>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
+    }
+
+    if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.s.flag)) return;
+
+    // ---- the last workgroup of the row: merge, then the cuts and the draw.
+    list_topk(sm.s, list, a.nchunks, k);
+
+    if ((tid >> 6) == 0) epilogue(a, R, sm.s, slot, k, greedy);
+    if (!LP) return;
+
+    // ---- raw logprobs of the sampled token and the raw top-K
+    __syncthreads();
+    if (raw_sel) list_topk(sm.s, a.raw_keys + (int64_t)slot * a.raw_stride, a.nchunks, K);
+    if ((tid >> 6) != 0) return;
+    const int lane = lane_id();
+    double L;
+    bool uniform;
+    combine_partials(a.partials + (int64_t)slot * a.partial_stride, a.nchunks, &L, &uniform);
+    if (lane == 0) {
+        const int32_t t = (int32_t)sm.s.flag;  // the sampled token, left by the epilogue
+        float lp = -INFINITY;
+        if (t >= 0 && t < V) lp = uniform ? (float)(-L) : (float)((double)sanitize(x[t]) - L);
+        a.lp_token[slot] = lp;
+    }
+    if (lane < K) {
+        const uint64_t key = sm.s.sel[lane];
+        const bool valid = key != 0ull;
+        a.lp_ids[(int64_t)slot * K + lane] = valid ? (int32_t)key_index(key) : -1;
+        a.lp_top[(int64_t)slot * K + lane] =
+            valid ? (uniform ? (float)(-L) : (float)((double)key_logit(key) - L)) : -INFINITY;
+    }
+}
+
+template <int EPT, bool VEC, bool LP>
 static int launch_t(const SampleArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((sample_kernel<EPT, VEC>), dim3((unsigned)(a.rows * a.nchunks)),
-                       dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((sample_kernel<EPT, VEC, LP>),
+                       dim3(grid_for(a.rows * a.nchunks, a.early_xcds)), dim3(kBlock), 0, s, a);
     return (int)hipGetLastError();
+}
+
+template <int EPT>
+static int launch_e(const SampleArgs &a, bool vec, hipStream_t s)
+{
+    if (a.lp_on) return vec ? launch_t<EPT, true, true>(a, s) : launch_t<EPT, false, true>(a, s);
+    return vec ? launch_t<EPT, true, false>(a, s) : launch_t<EPT, false, false>(a, s);
 }
 
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s)
 {
     switch (ept) {
-    case 4: return vec ? launch_t<4, true>(a, s) : launch_t<4, false>(a, s);
-    case 8: return vec ? launch_t<8, true>(a, s) : launch_t<8, false>(a, s);
-    case 16: return vec ? launch_t<16, true>(a, s) : launch_t<16, false>(a, s);
-    case 32: return vec ? launch_t<32, true>(a, s) : launch_t<32, false>(a, s);
+    case 4: return launch_e<4>(a, vec, s);
+    case 8: return launch_e<8>(a, vec, s);
+    case 16: return launch_e<16>(a, vec, s);
+    case 32: return launch_e<32>(a, vec, s);
     default: return (int)hipErrorInvalidValue;
     }
 }

@@ -46,19 +46,27 @@ struct ToLds {
     __device__ void put(int i, uint64_t v) const { p[i] = v; }
 };
 
+// A set of compacted candidates: four per-wave regions of kCap keys and
+// their counts.  The selection's own set lives in SelectSmem; a kernel that
+// keeps a second selection open at the same time brings another.
+struct Cands {
+    uint64_t *keys;  // [4 * kCap]
+    uint32_t *cnt;   // [4]
+};
+
+__device__ __forceinline__ Cands own_cands(SelectSmem &sm) { return Cands{sm.cand, sm.wave_cnt}; }
+
 // Each wave pads its region with zero keys up to a multiple of 8 (zero never
 // outranks a real key), so the rank loop reads eight keys per step.
-__device__ __forceinline__ void pad_region(SelectSmem &sm, int wave, uint32_t cnt)
+__device__ __forceinline__ void pad_region(Cands cd, int wave, uint32_t cnt)
 {
     const int lane = lane_id();
     const uint32_t end = (cnt + 7u) & ~7u;
-    if (cnt <= (uint32_t)kCap && cnt + (uint32_t)lane < end)
-        sm.cand[wave * kCap + cnt + lane] = 0ull;
+    if (cnt <= (uint32_t)kCap && cnt + (uint32_t)lane < end) cd.keys[wave * kCap + cnt + lane] = 0ull;
 }
 
 // Key at flat position f of the compacted candidates (regions in wave order).
-__device__ __forceinline__ uint64_t cand_at(const SelectSmem &sm, const uint32_t (&cnt)[4],
-                                            uint32_t f)
+__device__ __forceinline__ uint64_t cand_at(const uint64_t *keys, const uint32_t (&cnt)[4], uint32_t f)
 {
     uint32_t w = 0;
     if (f >= cnt[0]) {
@@ -68,24 +76,25 @@ __device__ __forceinline__ uint64_t cand_at(const SelectSmem &sm, const uint32_t
             if (f >= cnt[2]) { f -= cnt[2]; w = 3; }
         }
     }
-    return sm.cand[w * kCap + f];
+    return keys[w * kCap + f];
 }
 
 // Rank of every compacted candidate; writes the ones ranked below k to
 // out[rank] and zero-fills out[n..k) when fewer survived.  Each wave counts,
 // for every candidate, the larger keys in its own region only (eight LDS
-// reads per step); a barrier later the four partial counts are summed.
-// Requires every wave count <= kCap and padded regions.  Ends without a barrier.
+// reads per step); a barrier later the four partial counts (sm.part) are
+// summed.  Requires every wave count <= kCap and padded regions.  Ends
+// without a barrier.
 template <typename Out>
-__device__ __forceinline__ void rank_candidates(SelectSmem &sm, int k, Out out)
+__device__ __forceinline__ void rank_candidates(SelectSmem &sm, Cands cd, int k, Out out)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const uint32_t cnt[4] = {sm.wave_cnt[0], sm.wave_cnt[1], sm.wave_cnt[2], sm.wave_cnt[3]};
+    const uint32_t cnt[4] = {cd.cnt[0], cd.cnt[1], cd.cnt[2], cd.cnt[3]};
     const uint32_t n = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    const uint64_t *cw = sm.cand + wave * kCap;
+    const uint64_t *cw = cd.keys + wave * kCap;
     const uint32_t end = (cnt[wave] + 7u) & ~7u;
     for (uint32_t f = lane; f < n; f += 64) {
-        const uint64_t key = cand_at(sm, cnt, f);
+        const uint64_t key = cand_at(cd.keys, cnt, f);
         uint32_t r = 0;
         for (uint32_t j = 0; j < end; j += 8) {
             uint64_t c[8];
@@ -99,15 +108,15 @@ __device__ __forceinline__ void rank_candidates(SelectSmem &sm, int k, Out out)
     __syncthreads();
     for (uint32_t f = tid; f < n; f += kBlock) {
         const uint32_t rank = (uint32_t)sm.part[0][f] + sm.part[1][f] + sm.part[2][f] + sm.part[3][f];
-        if (rank < (uint32_t)k) out.put((int)rank, cand_at(sm, cnt, f));
+        if (rank < (uint32_t)k) out.put((int)rank, cand_at(cd.keys, cnt, f));
     }
     for (int r = (int)n + tid; r < k; r += kBlock) out.put(r, 0ull);
 }
 
-__device__ __forceinline__ bool any_overflow(const SelectSmem &sm)
+__device__ __forceinline__ bool any_overflow(Cands cd)
 {
-    return (sm.wave_cnt[0] > (uint32_t)kCap) | (sm.wave_cnt[1] > (uint32_t)kCap) |
-           (sm.wave_cnt[2] > (uint32_t)kCap) | (sm.wave_cnt[3] > (uint32_t)kCap);
+    return (cd.cnt[0] > (uint32_t)kCap) | (cd.cnt[1] > (uint32_t)kCap) |
+           (cd.cnt[2] > (uint32_t)kCap) | (cd.cnt[3] > (uint32_t)kCap);
 }
 
 // Block-wide maximum of one u64 per thread.  Ends after a barrier.
@@ -124,23 +133,25 @@ __device__ __forceinline__ uint64_t block_max_u64(SelectSmem &sm, uint64_t v)
     return m;
 }
 
-// Chunk selection over register-resident values.  v[e] holds the value of
-// element idx = base + (e/4)*1024 + tid*4 + e%4; ids >= V hold NaN.  Values
-// may be raw: NaN stands for -inf and +inf for the largest float, and both
-// are mapped when a key is formed.  Writes the chunk's top-k keys in order to
-// out[0..k).
+// Id of register element e of the calling thread in the chunk at `base`:
+// the chunk is read as EPT/4 coalesced passes of 1,024 ids, four per lane.
 template <int EPT>
 __device__ __forceinline__ uint32_t elem_index(int base, int e)
 {
     return (uint32_t)(base + (e >> 2) * 1024 + (int)threadIdx.x * 4 + (e & 3));
 }
 
-template <int EPT>
-__device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int base, int V, int k,
-                                           uint64_t *out_keys)
+// First half of a chunk selection: the threshold (the k-th largest of the
+// 256 lane maxima) and the ballot compaction of every value at or above it
+// into cd, whose regions are padded; ends after a barrier.  For k = 1 the
+// argmax is written to out[0] directly and true is returned (nothing left to
+// do); otherwise returns false.  In the degenerate case (fewer than k values
+// above -inf) every id below V is a candidate and v is sanitised in place.
+template <int EPT, typename Out>
+__device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], int base, int V,
+                                              int k, Cands cd, Out out)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const ToWorkspace out{out_keys};
     constexpr float kFltMax = 3.40282346638528859812e+38f;
 
     // fmaxf skips NaN, so the lane maximum is over the non-NaN values.
@@ -167,7 +178,7 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
         key = block_max_u64(sm, key);  // every thread of the block takes part
         if (key != 0ull) {
             if (tid == 0) out.put(0, key);
-            return;
+            return true;
         }
     }
 
@@ -186,7 +197,7 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
     }
 
     const uint64_t below = lanes_below_mask();
-    uint64_t *wc = sm.cand + wave * kCap;
+    uint64_t *wc = cd.keys + wave * kCap;
     uint32_t wcnt = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -199,16 +210,25 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
             wcnt += (uint32_t)__popcll(m);
         }
     }
-    if (lane == 0) sm.wave_cnt[wave] = wcnt;
-    pad_region(sm, wave, wcnt);
+    if (lane == 0) cd.cnt[wave] = wcnt;
+    pad_region(cd, wave, wcnt);
     __syncthreads();
+    return false;
+}
 
-    if (!any_overflow(sm)) {
-        rank_candidates(sm, k, out);
+// Second half: rank the compacted candidates, or, when a wave region
+// overflowed (massive ties), k argmax rounds over the register values, each
+// taking the best key strictly below the previous pick.  Uses sm.part, so a
+// barrier must separate it from the tail of an earlier rank.
+template <int EPT, typename Out>
+__device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EPT], int base, int V,
+                                             int k, Cands cd, Out out)
+{
+    const int tid = threadIdx.x;
+    if (!any_overflow(cd)) {
+        rank_candidates(sm, cd, k, out);
         return;
     }
-    // Fallback: k argmax rounds over the registers, each taking the best key
-    // strictly below the previous pick.
     uint64_t prev = ~0ull;
     for (int r = 0; r < k; ++r) {
         uint64_t best = 0;
@@ -224,6 +244,20 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
         if (tid == 0) out.put(r, best);
         prev = best;
     }
+}
+
+// Chunk selection over register-resident values.  v[e] holds the value of
+// element idx = base + (e/4)*1024 + tid*4 + e%4; ids >= V hold NaN.  Values
+// may be raw: NaN stands for -inf and +inf for the largest float, and both
+// are mapped when a key is formed.  Writes the chunk's top-k keys in order to
+// out_keys[0..k) with device-coherent stores.  Ends without a barrier.
+template <int EPT>
+__device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int base, int V, int k,
+                                           uint64_t *out_keys)
+{
+    const ToWorkspace out{out_keys};
+    if (chunk_compact<EPT>(sm, v, base, V, k, own_cands(sm), out)) return;
+    chunk_finish<EPT>(sm, v, base, V, k, own_cands(sm), out);
 }
 
 // Row merge: top-k of the chunk lists, written in order to sm.sel[0..k).
@@ -337,11 +371,11 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
         }
     }
     if (lane == 0) sm.wave_cnt[wave] = wcnt;
-    pad_region(sm, wave, wcnt);
+    pad_region(own_cands(sm), wave, wcnt);
     __syncthreads();
 
-    if (!any_overflow(sm)) {
-        rank_candidates(sm, k, ToLds{sm.sel});
+    if (!any_overflow(own_cands(sm))) {
+        rank_candidates(sm, own_cands(sm), k, ToLds{sm.sel});
         __syncthreads();
         return;
     }
@@ -365,6 +399,80 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
         prev = best;
     }
     __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Raw-logit log-softmax partials: per chunk (max, sum of exp(x - max)).
+// ---------------------------------------------------------------------------
+
+// Per-lane (max, sum) -> block (max, sum).  A lane whose values are all -inf
+// carries its element count as the sum (the uniform reading for an all -inf
+// domain); an empty lane carries (-inf, 0).  Ends after a barrier.
+__device__ __forceinline__ float2 block_max_sum(SelectSmem &sm, float m, float s)
+{
+    float *red = reinterpret_cast<float *>(sm.red);  // 8 floats
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const float wm = wave_max_f32(m);
+    if (lane == 0) red[wave] = wm;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float c;
+    if (M == -INFINITY) c = s;
+    else c = (m == -INFINITY) ? 0.0f : s * __expf(m - M);
+    c = wave_sum_f32(c);
+    if (lane == 0) red[4 + wave] = c;
+    __syncthreads();
+    const float S = (red[4] + red[5]) + (red[6] + red[7]);
+    __syncthreads();
+    return make_float2(M, S);
+}
+
+__device__ __forceinline__ void publish_partial(uint64_t *p, float2 ms)
+{
+    publish_u64(p, ((uint64_t)__float_as_uint(ms.y) << 32) | __float_as_uint(ms.x));
+}
+
+// Lane (max, sum) over EPT register values; NaN entries are skipped (ids past
+// V and NaN logits, which count as -inf); +inf counts as the largest float.
+// valid_count(): number of ids below V held by the lane, for the all -inf case.
+template <int EPT, typename ValidCount>
+__device__ __forceinline__ float2 lane_max_sum(const float (&v)[EPT], ValidCount valid_count)
+{
+    constexpr float kFltMax = 3.40282346638528859812e+38f;
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) m = (v[e] == v[e]) ? fmaxf(m, fminf(v[e], kFltMax)) : m;
+    float s = 0.0f;
+    if (m == -INFINITY) {
+        s = (float)valid_count();
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            s += (v[e] == v[e]) ? __expf(fminf(v[e], kFltMax) - m) : 0.0f;
+    }
+    return make_float2(m, s);
+}
+
+// Wave 0 of the merging workgroup: combine the row's chunk partials in fp64
+// in a fixed order.  L = M + log(S); an all -inf row is uniform (L = log n).
+__device__ __forceinline__ void combine_partials(const uint64_t *P, int nchunks, double *L,
+                                                 bool *uniform)
+{
+    const int lane = lane_id();
+    float mf = -INFINITY;
+    for (int c = lane; c < nchunks; c += 64)
+        mf = fmaxf(mf, __uint_as_float((uint32_t)read_published_u64(P + c)));
+    const double M = (double)wave_max_f32(mf);
+    double S = 0.0;
+    for (int c = lane; c < nchunks; c += 64) {
+        const uint64_t w = read_published_u64(P + c);
+        const float px = __uint_as_float((uint32_t)w), py = __uint_as_float((uint32_t)(w >> 32));
+        if (M == -INFINITY) S += (double)py;
+        else if (px != -INFINITY) S += (double)py * exp((double)px - M);
+    }
+    S = wave_sum_f64(S);
+    *uniform = (M == -INFINITY);
+    *L = *uniform ? log(S) : M + log(S);
 }
 
 }  // namespace rts

@@ -33,10 +33,10 @@ def to_dev(a, dtype=None):
     return t.cuda()
 
 
-def gpu_sample(logits, params, history=None, hist_len=None, logits_dev=None):
+def gpu_sample(logits, params, history=None, hist_len=None, logits_dev=None, logprobs=None):
     x = logits_dev if logits_dev is not None else to_dev(np.asarray(logits, np.float32))
     h = None if history is None else to_dev(np.asarray(history, np.int32))
-    out = R.sample_tokens(x, params, h, hist_len)
+    out = R.sample_tokens(x, params, h, hist_len, logprobs=logprobs)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -104,3 +104,26 @@ def compare_logprobs(g, o, tag=""):
         assert np.array_equal(np.isfinite(gl), fin), (where, "top_lp pad")
         assert np.all(np.abs(gl[fin] - ol[fin]) <= LP_ATOL), (where, "top_lp",
                                                              np.max(np.abs(gl[fin] - ol[fin])))
+
+
+def compare_fused_logprobs(g, o, logits, top_n, tag=""):
+    """Logprobs returned by a sampling call against the oracle's, row by row.
+    The top entries depend on the logits alone.  The token's logprob is the
+    oracle's for the oracle's own token; on a flagged row where the GPU drew
+    another kept id (allowed by the sampling bar), the oracle computes the
+    logprob of each of its kept ids and the GPU's token is looked up there."""
+    x = np.asarray(logits, np.float32)
+    ol = O.token_logprobs(x, o["token"], top_n)
+    B = x.shape[0]
+    same = g["token"] == o["token"]
+    gl = dict(token_lp=np.where(same, g["token_lp"], ol["token_lp"]), top_ids=g["top_ids"],
+              top_lp=g["top_lp"])
+    compare_logprobs(gl, ol, tag)
+    for r in np.nonzero(~same)[0]:
+        k = int(o["counts"][r, 0])
+        ids = o["kept_ids"][r][:k]
+        table = {int(i): O.token_logprobs_row(x[r], int(i), 0)["token_lp"] for i in ids}
+        t = int(g["token"][r])
+        assert t in table, (tag, r, "token outside the kept ids")
+        assert abs(float(g["token_lp"][r]) - table[t]) <= LP_ATOL, (tag, r, "token_lp")
+    return int(np.sum(~same))

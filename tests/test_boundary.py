@@ -43,10 +43,15 @@ def test_struct_layout_matches_header():
     fields = re.findall(r"^\s*(?:float|int32_t|uint64_t)\s+(\w+);", body, flags=re.M)
     assert fields == [f for f, _ in R.RowParams._fields_]
     assert ctypes.sizeof(R.RowParams) == 56
+    body = text[text.index("typedef struct rts_logprob_request"):
+                text.index("} rts_logprob_request;")]
+    fields = re.findall(r"^\s*(?:float|int32_t)\s*\*?\s*(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in R.LogprobRequest._fields_]
+    assert ctypes.sizeof(R.LogprobRequest) == 32
 
 
 def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws_bytes=BIG_WS,
-           history=None, H=0, ldh=0, hist_len=None):
+           history=None, H=0, ldh=0, hist_len=None, lp=None):
     L = R.lib()
     arr = R.row_params(params)
     B = len(params) if B is None else B
@@ -54,7 +59,8 @@ def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws
     if hist_len is not None:
         hl = (ctypes.c_int32 * len(hist_len))(*hist_len)
     return L.rts_sample_tokens(logits, B, V, V if ld is None else ld, arr, history, H, ldh, hl,
-                               token, None, None, None, None, None, 0, ws, ws_bytes, None)
+                               token, None, None, None, None, None, 0,
+                               None if lp is None else ctypes.byref(lp), ws, ws_bytes, None)
 
 
 SAMPLED = dict(temperature=0.7, top_k=20, top_p=0.9, min_p=0.05, seed=1, counter=0)
@@ -109,6 +115,30 @@ def test_bad_shapes_and_pointers():
     assert sample(rows, logits=None) == R.RTS_EINVAL and "logits" in last_error()
     assert sample(rows, token=None) == R.RTS_EINVAL and "token" in last_error()
     assert sample(rows, ws=None) == R.RTS_EINVAL
+
+
+@pytest.mark.parametrize("req,word", [
+    (dict(top_n=21), "top_n"),
+    (dict(top_n=-1), "top_n"),
+    (dict(reserved=2), "reserved"),
+    (dict(token_lp=None), "token_lp"),
+    (dict(top_ids=None), "top_ids"),
+    (dict(top_lp=None), "top_lp"),
+])
+def test_bad_logprob_request_is_refused(req, word):
+    full = dict(top_n=5, reserved=0, token_lp=4096, top_ids=4096, top_lp=4096)
+    full.update(req)
+    lp = R.LogprobRequest(**full)
+    assert sample([dict(SAMPLED)], lp=lp) == R.RTS_EINVAL
+    assert word in last_error(), last_error()
+
+
+def test_logprob_request_without_top_entries_needs_no_top_buffers():
+    # top_n = 0: NULL top buffers are fine; the call then fails later, on the
+    # bad row, which shows the request itself passed validation.
+    lp = R.LogprobRequest(top_n=0, reserved=0, token_lp=4096, top_ids=None, top_lp=None)
+    assert sample([dict(SAMPLED, top_k=0)], lp=lp) == R.RTS_EINVAL
+    assert "top_k" in last_error()
 
 
 def test_short_workspace():
