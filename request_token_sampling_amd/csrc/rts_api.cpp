@@ -305,7 +305,7 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
     const rts::WsLayout L = rts::ws_layout(rows_ws, V);
     base.keys = reinterpret_cast<uint64_t *>(ws + L.keys);
-    base.tickets = reinterpret_cast<uint32_t *>(ws + 256);
+    base.tickets = reinterpret_cast<uint32_t *>(ws + rts::kTicketRegion);
     base.token_lp = token_lp;
     base.top_ids = top_ids;
     base.top_lp = top_lp;

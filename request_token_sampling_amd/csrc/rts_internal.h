@@ -18,11 +18,16 @@ constexpr int kMaxTopN = 20;         // largest top_logprobs
 constexpr int kMinWavesPerSimd = 5;
 
 // Workspace layout (bytes from its start):
-//   [0, 256)     sampling tickets, one uint32 per row slot of a launch
-//   [256, 512)   logprob tickets
+//   [0, 8192)      sampling tickets, one per row slot of a launch, each on a
+//                  128-byte line of its own: a row's chunks all hit one
+//                  ticket, and rows sharing a line would queue behind each
+//                  other's atomics
+//   [8192, 16384)  logprob tickets, laid out the same way
 //   then, for every row slot of a launch: chunk candidate keys (64 per chunk),
 //   raw-logit top-K keys (20 per chunk) and (max, sum) partials (one per chunk)
-constexpr size_t kTicketBytes = 512;
+constexpr int kTicketStride = 32;  // uint32 words between two row slots' tickets
+constexpr size_t kTicketRegion = (size_t)kRowsPerLaunch * kTicketStride * 4u;
+constexpr size_t kTicketBytes = 2 * kTicketRegion;
 
 // Static LDS of the allowed-ids kernels besides their dynamic bitmap / list.
 constexpr size_t kAllowedStaticLds = 10240;

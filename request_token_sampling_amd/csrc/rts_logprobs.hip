@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
     if (K > 0) chunk_topk<EPT>(sm, v, base, V, K, list + (int64_t)chunk * K);
 
-    if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.flag)) return;
+    if (!take_last_ticket(&a.tickets[slot * kTicketStride], (uint32_t)a.nchunks, &sm.flag)) return;
 
     // ---- the last workgroup of the row.
     if (K > 0) list_topk(sm, list, a.nchunks, K);
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
         float lp = -INFINITY;
         if (t >= 0 && t < V) lp = uniform ? (float)(-L) : (float)((double)sanitize(x[t]) - L);
         a.token_lp[row] = lp;
-        a.tickets[slot] = 0u;
+        a.tickets[slot * kTicketStride] = 0u;
     }
     if (lane < K) {
         const uint64_t key = sm.sel[lane];

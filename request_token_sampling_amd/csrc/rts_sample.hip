@@ -71,7 +71,7 @@ __device__ __forceinline__ void load_chunk(const float *x, int base, int V, floa
 // The cuts and the draw, run by wave 0 of the row's last workgroup on the
 // merged kept sequence sm.sel[0..k).  Leaves the sampled token in sm.flag.
 __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
-                                         int slot, int k, bool greedy)
+                                         int slot, int k, bool greedy, uint64_t ctr, uint32_t x0)
 {
     const int lane = lane_id();
     const uint64_t key = (lane < k) ? sm.sel[lane] : 0ull;
@@ -82,20 +82,14 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     if (a.kept_logits) a.kept_logits[(int64_t)slot * kMaxK + lane] = y;
 
     const float y0 = lane_f32(y, 0);
-    // the row's Philox counter: device-resident when given (read here, then
-    // advanced below), else the caller's value from the argument block
-    const uint64_t ctr = a.counters ? a.counters[slot] : R.counter;
     int m = 1, n = 1, pick = 0;
-    uint32_t x0 = 0u;
     if (!greedy) {
-        // Everything that does not depend on the cuts first, so the fp64
-        // exponentials and the Philox rounds overlap: top_p weights
-        // exp(y - y0), tempered weights exp((y - y0) / T), and x0.
+        // Everything that does not depend on the cuts first: top_p weights
+        // exp(y - y0) and tempered weights exp((y - y0) / T).
         const double dy = (double)y - (double)y0;
         const bool head_masked = (y0 == -INFINITY);
         const double d = (lane < k && !head_masked) ? exp(dy) : 0.0;
         const double w = (lane < k && !head_masked) ? exp(dy / (double)R.temperature) : 0.0;
-        x0 = philox4x32_10_x0(ctr, R.seed);
         // min_p: keep the prefix with logit >= head + logf(min_p), in fp32.
         const float thr = y0 + R.lnp;
         m = __popcll(__ballot(lane < k && y >= thr));
@@ -132,7 +126,7 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
         }
         if (a.philox_x0) a.philox_x0[slot] = x0;
         if (a.counters) a.counters[slot] = ctr + (uint64_t)a.counter_stride;
-        a.tickets[slot] = 0u;  // ready for the next launch on this workspace
+        a.tickets[slot * kTicketStride] = 0u;  // ready for the next launch on this workspace
     }
 }
 
@@ -227,12 +221,19 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         chunk_finish<EPT>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
     }
 
-    if (!take_last_ticket(&a.tickets[slot], (uint32_t)a.nchunks, &sm.s.flag)) return;
+    if (!take_last_ticket(&a.tickets[slot * kTicketStride], (uint32_t)a.nchunks, &sm.s.flag)) return;
 
     // ---- the last workgroup of the row: merge, then the cuts and the draw.
-    list_topk(sm.s, list, a.nchunks, k);
+    // The row's Philox counter (device-resident when given, else the
+    // caller's value) and the draw's word x0 depend on neither, so they are
+    // computed while the merge's first loads are in flight.
+    const uint64_t ctr = a.counters ? a.counters[slot] : R.counter;
+    uint32_t x0 = 0u;
+    list_topk(sm.s, list, a.nchunks, k, [&]() {
+        if (!greedy) x0 = philox4x32_10_x0(ctr, R.seed);
+    });
 
-    if ((tid >> 6) == 0) epilogue(a, R, sm.s, slot, k, greedy);
+    if ((tid >> 6) == 0) epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
     if (!LP) return;
 
     // ---- raw logprobs of the sampled token and the raw top-K

@@ -313,7 +313,15 @@ __device__ __forceinline__ void load_stream_batch(const uint64_t *list, int k, c
     }
 }
 
-__device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, int C, int k)
+struct NoWork {
+    __device__ void operator()() const {}
+};
+
+// `overlap` runs once the first loads are in flight, so independent work of
+// the caller hides behind their latency.
+template <typename Overlap = NoWork>
+__device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, int C, int k,
+                                          Overlap overlap = NoWork{})
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const MergeStreams ms = merge_streams(C, k);
@@ -321,6 +329,7 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
     // pass 1: the first batch of the first stream (kept), heads of the others
     uint64_t first[kBatch];
     load_stream_batch(list, k, ms, ms.c0, ms.nstreams > 0, 0, first);
+    overlap();
     uint64_t lm = first[0];
     for (int si = 1; si < ms.max_streams; ++si) {
         const int c = ms.c0 + si * ms.cstride;
