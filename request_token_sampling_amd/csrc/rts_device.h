@@ -182,6 +182,77 @@ __device__ __forceinline__ float wave_sum_f32(float x)
     return lane_f32(s, 63);
 }
 
+// The value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}: DPP quad
+// permutes for 1 and 2, row shifts for 4, a row rotation for 8, an LDS-free
+// swizzle within 32 lanes for 16 and a lane permute for 32.
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x)
+{
+    if constexpr (J == 1) {
+        return dpp_u64<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+    } else if constexpr (J == 2) {
+        return dpp_u64<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+    } else if constexpr (J == 4) {
+        const uint64_t up = dpp_u64<0x104>(x), down = dpp_u64<0x114>(x);  // row_shl:4, row_shr:4
+        return (lane_id() & 4) ? down : up;
+    } else if constexpr (J == 8) {
+        return dpp_u64<0x128>(x);  // row_ror:8
+    } else if constexpr (J == 16) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)x, 0x401F);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(x >> 32), 0x401F);
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        static_assert(J == 32, "lane distance");
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, 32);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), 32);
+        return ((uint64_t)hi << 32) | lo;
+    }
+}
+
+// Bitonic sort, descending, of one (ONE) or two (x1 = element lane + 64)
+// u64 keys per lane across the wave (Batcher's network: sizes 2..N, each a
+// merge of distance SIZE/2 .. 1).  Zero keys sink to the end.
+__device__ __forceinline__ uint64_t keep(uint64_t x, uint64_t y, bool take_max)
+{
+    return ((x > y) == take_max) ? x : y;
+}
+
+template <int SIZE, int J, bool TWO>
+__device__ __forceinline__ void bitonic_steps(uint64_t &x0, uint64_t &x1)
+{
+    const int lane = lane_id();
+    const bool lower = (lane & J) == 0;
+    const bool d0 = (lane & SIZE) == 0, d1 = ((lane + 64) & SIZE) == 0;
+    const uint64_t y0 = xor_lane_u64<J>(x0);
+    if constexpr (TWO) {
+        const uint64_t y1 = xor_lane_u64<J>(x1);
+        x1 = keep(x1, y1, d1 == lower);
+    }
+    x0 = keep(x0, y0, d0 == lower);
+    if constexpr (J > 1) bitonic_steps<SIZE, J / 2, TWO>(x0, x1);
+}
+
+template <int SIZE, bool TWO>
+__device__ __forceinline__ void bitonic_sizes(uint64_t &x0, uint64_t &x1)
+{
+    bitonic_steps<SIZE, SIZE / 2, TWO>(x0, x1);
+    if constexpr (SIZE < 64) bitonic_sizes<SIZE * 2, TWO>(x0, x1);
+}
+
+template <bool TWO>
+__device__ __forceinline__ void wave_sort_desc(uint64_t &x0, uint64_t &x1)
+{
+    bitonic_sizes<2, TWO>(x0, x1);
+    if constexpr (TWO) {
+        // size 128: x0 holds elements 0..63 (a descending run), x1 elements
+        // 64..127 (ascending): one in-lane step, then distances 32 .. 1
+        const uint64_t hi = x0 > x1 ? x0 : x1, lo = x0 > x1 ? x1 : x0;
+        x0 = hi;
+        x1 = lo;
+        bitonic_steps<128, 32, true>(x0, x1);
+    }
+}
+
 // Largest t (to `bits` leading bits) with #{keys >= t} >= k, over the four
 // keys a[0..3] held by each lane of the wave (256 keys).  Every wave that runs
 // this on the same keys gets the same t, so no broadcast is needed.
@@ -195,6 +266,27 @@ __device__ __forceinline__ uint32_t kth_largest_key_256(const uint32_t a[4], int
         const int cnt = __popcll(__ballot(a[0] >= c)) + __popcll(__ballot(a[1] >= c)) +
                         __popcll(__ballot(a[2] >= c)) + __popcll(__ballot(a[3] >= c));
         if (cnt >= k) t = c;
+    }
+    return t;
+}
+
+// The same t, two bits per step: the three thresholds of a step are counted
+// together, so the dependent chain is half as long.
+template <int BITS>
+__device__ __forceinline__ uint32_t kth_largest_key_256_q(const uint32_t a[4], int k)
+{
+    static_assert(BITS % 2 == 0, "two bits per step");
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = 30; b >= 32 - BITS; b -= 2) {
+        const uint32_t c1 = t | (1u << b), c2 = t | (2u << b), c3 = t | (3u << b);
+        const int n1 = __popcll(__ballot(a[0] >= c1)) + __popcll(__ballot(a[1] >= c1)) +
+                       __popcll(__ballot(a[2] >= c1)) + __popcll(__ballot(a[3] >= c1));
+        const int n2 = __popcll(__ballot(a[0] >= c2)) + __popcll(__ballot(a[1] >= c2)) +
+                       __popcll(__ballot(a[2] >= c2)) + __popcll(__ballot(a[3] >= c2));
+        const int n3 = __popcll(__ballot(a[0] >= c3)) + __popcll(__ballot(a[1] >= c3)) +
+                       __popcll(__ballot(a[2] >= c3)) + __popcll(__ballot(a[3] >= c3));
+        t = (n3 >= k) ? c3 : (n2 >= k) ? c2 : (n1 >= k) ? c1 : t;
     }
     return t;
 }

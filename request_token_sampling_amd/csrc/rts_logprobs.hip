@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
         const float tf = key_threshold(kth_largest_key_256<16>(lk, K));
         const uint64_t below = lanes_below_mask();
-        uint64_t *wc = sm.cand + wave * kCap;
+        uint64_t *wc = sm.cand + wave * kRegion;
         uint32_t wcnt = 0;
 #pragma unroll
         for (int j = 0; j < kAllowedPerThread; ++j) {

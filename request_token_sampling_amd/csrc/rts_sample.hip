@@ -25,7 +25,7 @@ struct SampleSmem {
     SelectSmem s;
     uint32_t pen_bits[EPT * kBlock / 32];  // one bit per id of the chunk
     uint32_t pen_cnt[EPT * kBlock / 2];    // two 16-bit counts per word
-    uint64_t raw_keys[LP ? 4 * kCap : 1];  // candidates of the raw top-K
+    uint64_t raw_keys[LP ? 4 * kRegion : 1];  // candidates of the raw top-K
     uint32_t raw_cnt[4];
 };
 
@@ -181,10 +181,15 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     }
 
     if (n_eff > 0) {
+        // Clear the chunk's bits and only the count words the window touches.
         for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
-        for (int w = tid; w < CH / 2; w += kBlock) sm.pen_cnt[w] = 0u;
-        __syncthreads();
         const int32_t *h = a.history + R.hist_off;
+        for (int j = tid; j < n_eff; j += kBlock) {
+            const int32_t id = h[j];
+            const int rel = id - base;
+            if (id >= 0 && id < V && rel >= 0 && rel < CH) sm.pen_cnt[rel >> 1] = 0u;
+        }
+        __syncthreads();
         for (int j = tid; j < n_eff; j += kBlock) {
             const int32_t id = h[j];
             const int rel = id - base;

@@ -22,15 +22,16 @@
 
 namespace rts {
 
-constexpr int kCap = 128;  // LDS candidate slots per wave
+constexpr int kCap = 128;          // LDS candidate slots per wave
+constexpr int kRegion = kCap + 8;  // region stride; the extra slots absorb overflowing writes
 
 struct SelectSmem {
     uint32_t lane_keys[kBlock];
     uint32_t wave_cnt[4];
     uint32_t flag;
-    uint32_t pad;
+    uint32_t thr;  // a chunk selection's threshold key, broadcast by wave 0
     uint64_t red[4];
-    uint64_t cand[4 * kCap];
+    uint64_t cand[4 * kRegion];
     uint64_t sel[kMaxK];
     uint16_t part[4][4 * kCap];  // partial ranks, one row per wave
 };
@@ -46,23 +47,27 @@ struct ToLds {
     __device__ void put(int i, uint64_t v) const { p[i] = v; }
 };
 
-// A set of compacted candidates: four per-wave regions of kCap keys and
+// A set of compacted candidates: four per-wave regions of up to kCap keys and
 // their counts.  The selection's own set lives in SelectSmem; a kernel that
 // keeps a second selection open at the same time brings another.
 struct Cands {
-    uint64_t *keys;  // [4 * kCap]
+    uint64_t *keys;  // [4 * kRegion], region w at w * kRegion
     uint32_t *cnt;   // [4]
 };
 
 __device__ __forceinline__ Cands own_cands(SelectSmem &sm) { return Cands{sm.cand, sm.wave_cnt}; }
 
-// Each wave pads its region with zero keys up to a multiple of 8 (zero never
-// outranks a real key), so the rank loop reads eight keys per step.
+// Regions are padded with zero keys (zero never outranks a real key) to a
+// multiple of kPad, so the rank loop reads kPad keys per step.
+constexpr uint32_t kPad = 8;
+
+__device__ __forceinline__ uint32_t padded(uint32_t cnt) { return (cnt + kPad - 1u) & ~(kPad - 1u); }
+
 __device__ __forceinline__ void pad_region(Cands cd, int wave, uint32_t cnt)
 {
     const int lane = lane_id();
-    const uint32_t end = (cnt + 7u) & ~7u;
-    if (cnt <= (uint32_t)kCap && cnt + (uint32_t)lane < end) cd.keys[wave * kCap + cnt + lane] = 0ull;
+    if (cnt <= (uint32_t)kCap && cnt + (uint32_t)lane < padded(cnt))
+        cd.keys[wave * kRegion + cnt + lane] = 0ull;
 }
 
 // Key at flat position f of the compacted candidates (regions in wave order).
@@ -76,14 +81,14 @@ __device__ __forceinline__ uint64_t cand_at(const uint64_t *keys, const uint32_t
             if (f >= cnt[2]) { f -= cnt[2]; w = 3; }
         }
     }
-    return keys[w * kCap + f];
+    return keys[w * kRegion + f];
 }
 
 // Rank of every compacted candidate; writes the ones ranked below k to
 // out[rank] and zero-fills out[n..k) when fewer survived.  Each wave counts,
-// for every candidate, the larger keys in its own region only (eight LDS
-// reads per step); a barrier later the four partial counts (sm.part) are
-// summed.  Requires every wave count <= kCap and padded regions.  Ends
+// for every candidate, the larger keys in its own region only (kPad LDS
+// reads per step, shared by two candidates per lane); a barrier later the
+// four partial counts (sm.part) are summed.  Requires every wave count <= kCap and padded regions.  Ends
 // without a barrier.
 template <typename Out>
 __device__ __forceinline__ void rank_candidates(SelectSmem &sm, Cands cd, int k, Out out)
@@ -91,19 +96,26 @@ __device__ __forceinline__ void rank_candidates(SelectSmem &sm, Cands cd, int k,
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const uint32_t cnt[4] = {cd.cnt[0], cd.cnt[1], cd.cnt[2], cd.cnt[3]};
     const uint32_t n = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    const uint64_t *cw = cd.keys + wave * kCap;
-    const uint32_t end = (cnt[wave] + 7u) & ~7u;
-    for (uint32_t f = lane; f < n; f += 64) {
-        const uint64_t key = cand_at(cd.keys, cnt, f);
-        uint32_t r = 0;
-        for (uint32_t j = 0; j < end; j += 8) {
-            uint64_t c[8];
+    const uint64_t *cw = cd.keys + wave * kRegion;
+    const uint32_t end = padded(cnt[wave]);
+    // two candidates per lane and pass, so up to 128 take one pass over the region
+    for (uint32_t f = lane; f < n; f += 128) {
+        const bool two = f + 64 < n;
+        const uint64_t key0 = cand_at(cd.keys, cnt, f);
+        const uint64_t key1 = two ? cand_at(cd.keys, cnt, f + 64) : ~0ull;
+        uint32_t r0 = 0, r1 = 0;
+        for (uint32_t j = 0; j < end; j += kPad) {
+            uint64_t c[kPad];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) c[u] = cw[j + u];
+            for (uint32_t u = 0; u < kPad; ++u) c[u] = cw[j + u];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) r += (c[u] > key) ? 1u : 0u;
+            for (uint32_t u = 0; u < kPad; ++u) {
+                r0 += (c[u] > key0) ? 1u : 0u;
+                r1 += (c[u] > key1) ? 1u : 0u;
+            }
         }
-        sm.part[wave][f] = (uint16_t)r;
+        sm.part[wave][f] = (uint16_t)r0;
+        if (two) sm.part[wave][f + 64] = (uint16_t)r1;
     }
     __syncthreads();
     for (uint32_t f = tid; f < n; f += kBlock) {
@@ -111,6 +123,20 @@ __device__ __forceinline__ void rank_candidates(SelectSmem &sm, Cands cd, int k,
         if (rank < (uint32_t)k) out.put((int)rank, cand_at(cd.keys, cnt, f));
     }
     for (int r = (int)n + tid; r < k; r += kBlock) out.put(r, 0ull);
+}
+
+// n <= 128 compacted candidates, sorted by the calling wave alone: lane l
+// returns the key of rank l (zero past n).
+__device__ __forceinline__ uint64_t wave_sorted_candidates(const uint64_t *keys,
+                                                          const uint32_t (&cnt)[4])
+{
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t n = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint64_t x0 = lane < n ? cand_at(keys, cnt, lane) : 0ull;
+    uint64_t x1 = lane + 64u < n ? cand_at(keys, cnt, lane + 64u) : 0ull;
+    if (n > 64u) wave_sort_desc<true>(x0, x1);
+    else wave_sort_desc<false>(x0, x1);
+    return x0;
 }
 
 __device__ __forceinline__ bool any_overflow(Cands cd)
@@ -184,10 +210,15 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
 
     sm.lane_keys[tid] = (lmax != lmax) ? 0u : value_key(lmax);
     __syncthreads();
-
-    const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
-                            sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-    const float tf = key_threshold(kth_largest_key_256<16>(lk, k));
+    // One wave finds the threshold; the others would only repeat its work.
+    if (wave == 0) {
+        const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
+                                sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
+        const uint32_t t = kth_largest_key_256_q<16>(lk, k);
+        if (lane == 0) sm.thr = t;
+    }
+    __syncthreads();
+    const float tf = key_threshold(sm.thr);
     if (tf == -INFINITY) {
         // Degenerate chunk (fewer than k values above -inf): every id below V
         // is a candidate, NaN counting as -inf.
@@ -196,22 +227,43 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
             v[e] = ((int)elem_index<EPT>(base, e) < V) ? sanitize(v[e]) : __builtin_nanf("");
     }
 
-    const uint64_t below = lanes_below_mask();
-    uint64_t *wc = cd.keys + wave * kCap;
+    // Ballot compaction of the raw entries (float bits, id): the slot is the
+    // wave's running count plus the lanes below that also pass; slots past
+    // kCap land in the region's spare slots (the region has then overflowed
+    // and its contents are not used).
+    uint64_t *wc = cd.keys + wave * kRegion;
+    const uint32_t ibase = (uint32_t)(base + tid * 4);
     uint32_t wcnt = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         const bool c = v[e] >= tf;
         const uint64_t m = __ballot(c);
         if (m) {
-            const uint32_t pos = wcnt + (uint32_t)__popcll(m & below);
-            if (c && pos < (uint32_t)kCap)
-                wc[pos] = cand_key(fminf(v[e], kFltMax), elem_index<EPT>(base, e));
+            uint32_t pos = wcnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            pos = pos < (uint32_t)kCap ? pos : (uint32_t)kCap;
+            const uint32_t idx = ibase + (uint32_t)((e >> 2) * 1024 + (e & 3));
+            if (c) wc[pos] = ((uint64_t)__float_as_uint(v[e]) << 32) | idx;
             wcnt += (uint32_t)__popcll(m);
         }
     }
     if (lane == 0) cd.cnt[wave] = wcnt;
-    pad_region(cd, wave, wcnt);
+    // The wave turns its own entries into keys and pads the region with zero
+    // keys to a multiple of kPad; one wave's LDS accesses stay in order, so
+    // this needs no workgroup barrier.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t nk = wcnt < (uint32_t)kCap ? wcnt : (uint32_t)kCap;
+    const uint32_t end = padded(nk);
+    for (uint32_t j = (uint32_t)lane; j < end; j += 64) {
+        uint64_t key = 0ull;
+        if (j < nk) {
+            const uint64_t r = wc[j];
+            key = cand_key(fminf(__uint_as_float((uint32_t)(r >> 32)), kFltMax), (uint32_t)r);
+        }
+        wc[j] = key;
+    }
     __syncthreads();
     return false;
 }
@@ -226,6 +278,15 @@ __device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EP
 {
     const int tid = threadIdx.x;
     if (!any_overflow(cd)) {
+        const uint32_t cnt[4] = {cd.cnt[0], cd.cnt[1], cd.cnt[2], cd.cnt[3]};
+        if (cnt[0] + cnt[1] + cnt[2] + cnt[3] <= 128u) {
+            // few candidates: wave 0 sorts them alone and writes the top k
+            if ((tid >> 6) == 0) {
+                const uint64_t key = wave_sorted_candidates(cd.keys, cnt);
+                if (lane_id() < k) out.put(lane_id(), key);
+            }
+            return;
+        }
         rank_candidates(sm, cd, k, out);
         return;
     }
@@ -268,7 +329,9 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
 // are the top ranks of every chunk; the k-th largest of them is then close to
 // the row's k-th key.  With more chunks each lane owns whole chunks t, t + 256,
 // ...  A lane stops reading a stream at its first key below the threshold.
-// Loads are device-coherent and issued eight at a time.  Ends after a barrier.
+// Loads are device-coherent and issued eight at a time.  On return sm.sel is
+// valid in wave 0 (in every wave only when the call ended with a barrier,
+// which callers must not rely on).
 constexpr int kBatch = 8;
 
 struct MergeStreams {
@@ -348,11 +411,11 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
     __syncthreads();
     const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                             sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-    const uint64_t t64 = (uint64_t)kth_largest_key_256<16>(lk, k) << 32;
+    const uint64_t t64 = (uint64_t)kth_largest_key_256_q<16>(lk, k) << 32;
 
     // pass 2: walk every stream while its keys reach the threshold
     const uint64_t below = lanes_below_mask();
-    uint64_t *wc = sm.cand + wave * kCap;
+    uint64_t *wc = sm.cand + wave * kRegion;
     uint32_t wcnt = 0;
     for (int si = 0; si < ms.max_streams; ++si) {
         const int c = ms.c0 + si * ms.cstride;
@@ -384,6 +447,19 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
     __syncthreads();
 
     if (!any_overflow(own_cands(sm))) {
+        const uint32_t cnt[4] = {sm.wave_cnt[0], sm.wave_cnt[1], sm.wave_cnt[2], sm.wave_cnt[3]};
+        if (cnt[0] + cnt[1] + cnt[2] + cnt[3] <= 128u) {
+            // Few candidates: wave 0 sorts them on its own, with no further
+            // barrier; the other waves are done.
+            if (wave == 0) {
+                const uint64_t key = wave_sorted_candidates(sm.cand, cnt);
+                if (lane < k) sm.sel[lane] = key;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            return;
+        }
         rank_candidates(sm, own_cands(sm), k, ToLds{sm.sel});
         __syncthreads();
         return;
