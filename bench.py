@@ -210,11 +210,41 @@ def roofline(wl, kern_ms):
                 per_call_us={l: round(m * 1e3, 3) for l, m in zip(wl.labels, kern_ms)})
 
 
+def read_floor(wl, launches=400):
+    """The practical bandwidth floor beside the roofline: rts_read_rows (the
+    sampler's grid, chunking and loads with only a chunk maximum) over the
+    same rotating copies, replayed from a captured graph; per-launch time."""
+    import request_token_sampling_amd as R
+    torch = wl.torch
+    rc = R.ReadCall(wl.copies[0])
+
+    def launch(i):
+        rc.logits = wl.copies[i % wl.ncopies]
+        rc()
+
+    launch(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(launches):
+            launch(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / launches * 1e6
+    del graph
+    gbs = wl.B * wl.row_bytes / (us * 1e-6) / 1e9
+    return dict(kernel="rts::read_rows_kernel", us_per_launch=round(us, 3), achieved=round(gbs, 1),
+                frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
 def measure(wl, steps, warmup):
     eager = time_eager(wl, steps, warmup)
     graph = time_graph(wl, steps)
     kern = kernel_durations(wl, min(steps, 500))
-    return dict(graph_wall=graph, eager_wall=eager, kern_ms=kern)
+    return dict(graph_wall=graph, eager_wall=eager, kern_ms=kern, floor=read_floor(wl))
 
 
 def read_traffic(workload):
@@ -406,7 +436,7 @@ def main():
                    "passes_per_step": wl.passes, "launch": "hip_graph_replay",
                    "philox_counters": "device-resident, advanced per call",
                    "logit_copies_rotated": wl.ncopies, "device": props.name},
-        "roofline": roofline(wl, m["kern_ms"]),
+        "roofline": dict(roofline(wl, m["kern_ms"]), read_floor=m["floor"]),
         "eager": {"value": round(wl.sampled_rows * args.steps / m["eager_wall"], 1),
                   "ms_per_step": round(m["eager_wall"] / args.steps * 1e3, 5)},
     }
@@ -424,7 +454,8 @@ def main():
                                unit="rows/s", steps=steps,
                                ms_per_step=round(m2["graph_wall"] / steps * 1e3, 5),
                                eager_ms_per_step=round(m2["eager_wall"] / steps * 1e3, 5),
-                               roofline=roofline(w2, m2["kern_ms"]), desc=w2.desc,
+                               roofline=dict(roofline(w2, m2["kern_ms"]), read_floor=m2["floor"]),
+                               desc=w2.desc,
                                passes_per_step=w2.passes)
             del w2
             torch.cuda.empty_cache()

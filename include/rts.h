@@ -164,6 +164,22 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
                        float *token_lp, int32_t *top_ids, float *top_lp,
                        void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * A plain streaming read of the rows, the measuring stick for the sampler's
+ * bandwidth: the same grid, chunking, 16-byte loads and row-major layout as
+ * rts_sample_tokens over the same B rows, with only a maximum taken per
+ * chunk and no selection, merge or draw.  Its duration is the practical
+ * floor of any one-pass kernel over those bytes.
+ *   logits     device fp32 [B][ld] as in rts_sample_tokens.
+ *   chunk_max  device fp32 [B][ceil(V / 1024)]; row r's first C entries
+ *              receive its chunk maxima (C = the sampler's chunk count for
+ *              this B and V), NaN ignored.
+ * Errors: RTS_EINVAL for bad shapes or NULL pointers; RTS_EDEVICE if the
+ * launch fails.  B = 0 is a no-op.
+ */
+int rts_read_rows(const float *logits, int64_t B, int64_t V, int64_t ld, float *chunk_max,
+                  hipStream_t stream);
+
 /* Static description of an error code. */
 const char *rts_strerror(int code);
 

@@ -86,8 +86,9 @@ def lib() -> ctypes.CDLL:
         L.rts_sample_tokens.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P, P, P,
                                         I64, P, P, SZ, P]
         L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
+        L.rts_read_rows.argtypes = [P, I64, I64, I64, P, P]
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
-                  "rts_token_logprobs"):
+                  "rts_token_logprobs", "rts_read_rows"):
             getattr(L, f).restype = ctypes.c_int
         L.rts_strerror.argtypes = [ctypes.c_int]
         L.rts_strerror.restype = ctypes.c_char_p
@@ -284,5 +285,22 @@ def token_logprobs(logits, tokens, top_n: int, allowed=None, allowed_off=None,
                        stream)().results()
 
 
+class ReadCall:
+    """One prepared call of rts_read_rows, the plain streaming read of the
+    rows used as the sampler's bandwidth measuring stick."""
+
+    def __init__(self, logits, stream=None):
+        self.logits, self.B, self.V, self.ld = _rows_view(logits)
+        self.chunk_max = torch.full((self.B, (self.V + 1023) // 1024), float("nan"),
+                                    dtype=torch.float32, device=self.logits.device)
+        self.stream = stream
+
+    def __call__(self):
+        _check(lib().rts_read_rows(self.logits.data_ptr(), self.B, self.V, self.ld,
+                                   self.chunk_max.data_ptr(), _stream_handle(self.stream)))
+        return self
+
+
 __all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
-           "make_workspace", "row_params", "RowParams", "LogprobRequest", "RTSError", "lib"]
+           "make_workspace", "row_params", "RowParams", "LogprobRequest", "ReadCall", "RTSError",
+           "lib"]

@@ -358,4 +358,29 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     return RTS_OK;
 }
 
+int rts_read_rows(const float *logits, int64_t B, int64_t V, int64_t ld, float *chunk_max,
+                  hipStream_t stream)
+{
+    clear_error();
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (B == 0) return RTS_OK;
+    if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
+    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
+    if (logits == nullptr || chunk_max == nullptr)
+        return fail(RTS_EINVAL, "logits and chunk_max must not be NULL");
+    const int out_stride = (int)rts::max_chunks(V);
+    for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
+        const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
+        const int ept = choose_ept(rows, V);
+        const int nchunks = (int)chunks_for(V, ept);
+        const int e = rts::launch_read_rows(logits + r0 * ld, rows, (int)V, ld, nchunks, out_stride,
+                                            chunk_max + r0 * out_stride, ept,
+                                            is_vec_ok(logits + r0 * ld, ld),
+                                            rows * nchunks <= rts::kEarlyXcdWork, stream);
+        if (e != 0) return fail(RTS_EDEVICE, "read launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    return RTS_OK;
+}
+
 }  // extern "C"

@@ -146,5 +146,7 @@ int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s);
 int launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
+int launch_read_rows(const float *x, int rows, int V, int64_t ld, int nchunks, int out_stride,
+                     float *out, int ept, bool vec, bool early, hipStream_t s);
 
 }  // namespace rts

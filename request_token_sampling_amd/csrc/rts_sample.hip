@@ -290,6 +290,55 @@ int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s)
     }
 }
 
+// The streaming-read measuring stick: the sampler's grid, chunking and loads,
+// with only a chunk maximum computed.
+template <int EPT, bool VEC>
+__global__ __launch_bounds__(kBlock) void read_rows_kernel(const float *x0, int rows, int V, int64_t ld,
+                                                          int nchunks, int out_stride, float *out,
+                                                          int early)
+{
+    const int lb = logical_block(early);
+    if (lb < 0 || lb >= rows * nchunks) return;
+    const int row = lb / nchunks, chunk = lb - row * nchunks;
+    float v[EPT];
+    load_chunk<EPT, VEC>(x0 + (int64_t)row * ld, chunk * EPT * kBlock, V, v);
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) m = fmaxf(m, v[e]);
+    m = wave_max_f32(m);
+    __shared__ float red[4];
+    if (lane_id() == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        out[(int64_t)row * out_stride + chunk] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int EPT>
+static void launch_read_t(const float *x, int rows, int V, int64_t ld, int nchunks, int out_stride,
+                          float *out, bool vec, bool early, hipStream_t s)
+{
+    const dim3 g(grid_for(rows * nchunks, early ? 1 : 0));
+    if (vec)
+        hipLaunchKernelGGL((read_rows_kernel<EPT, true>), g, dim3(kBlock), 0, s, x, rows, V, ld,
+                           nchunks, out_stride, out, early ? 1 : 0);
+    else
+        hipLaunchKernelGGL((read_rows_kernel<EPT, false>), g, dim3(kBlock), 0, s, x, rows, V, ld,
+                           nchunks, out_stride, out, early ? 1 : 0);
+}
+
+int launch_read_rows(const float *x, int rows, int V, int64_t ld, int nchunks, int out_stride,
+                     float *out, int ept, bool vec, bool early, hipStream_t s)
+{
+    switch (ept) {
+    case 4: launch_read_t<4>(x, rows, V, ld, nchunks, out_stride, out, vec, early, s); break;
+    case 8: launch_read_t<8>(x, rows, V, ld, nchunks, out_stride, out, vec, early, s); break;
+    case 16: launch_read_t<16>(x, rows, V, ld, nchunks, out_stride, out, vec, early, s); break;
+    case 32: launch_read_t<32>(x, rows, V, ld, nchunks, out_stride, out, vec, early, s); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
 __global__ void zero_u32_kernel(uint32_t *p, size_t n)
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -202,3 +202,13 @@ def test_strerror():
     L = R.lib()
     for code in (0, -1, -2, -3, 7):
         assert L.rts_strerror(code)
+
+
+def test_read_rows_refusals():
+    L = R.lib()
+    assert L.rts_read_rows(FAKE, -1, 100, 100, FAKE, None) == R.RTS_EINVAL
+    assert L.rts_read_rows(FAKE, 0, 100, 100, FAKE, None) == R.RTS_OK
+    assert L.rts_read_rows(FAKE, 1, 0, 100, FAKE, None) == R.RTS_EINVAL
+    assert L.rts_read_rows(FAKE, 1, 100, 99, FAKE, None) == R.RTS_EINVAL and "ld" in last_error()
+    assert L.rts_read_rows(None, 1, 100, 100, FAKE, None) == R.RTS_EINVAL
+    assert L.rts_read_rows(FAKE, 1, 100, 100, None, None) == R.RTS_EINVAL

@@ -326,3 +326,18 @@ def test_graph_replay_draws_fresh_numbers():
         torch.cuda.synchronize()
     assert len(seen) == 3, "every replay must draw a fresh number"
     assert np.array_equal(ctr.cpu().numpy(), c0 + 3)
+
+
+@pytest.mark.parametrize("B,Vx", [(1, V), (40, V), (3, 10007)])
+def test_read_rows_measuring_stick(B, Vx):
+    """The streaming-read kernel bench.py times as the bandwidth floor reads
+    every element once: its chunk maxima are the rows' maxima, exactly."""
+    rng = np.random.default_rng(B + Vx)
+    x = rng.normal(0, 3, (B, Vx)).astype(np.float32)
+    say("case read rows", B, Vx)
+    call = R.ReadCall(to_dev(x))()
+    torch.cuda.synchronize()
+    cm = call.chunk_max.cpu().numpy()
+    nch = int(np.sum(~np.isnan(cm[0])))             # entries past the chunk count stay NaN
+    assert nch >= 1
+    assert np.array_equal(np.max(cm[:, :nch], axis=1), np.max(x, axis=1))
