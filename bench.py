@@ -131,15 +131,11 @@ class Workload:
         self.passes = [l for l in self.labels] + (["logprobs_allowed"] if self.lp_calls else [])
         self.torch = torch
 
-    def step(self, i, events=None):
+    def step(self, i):
         x = self.copies[i % self.ncopies]
-        for j, c in enumerate(self.calls):
+        for c in self.calls:
             c.logits = x
-            if events is not None:
-                events[j][0].record()
             c()
-            if events is not None:
-                events[j][1].record()
         for c in self.lp_calls:
             c.logits = x
             c()
@@ -179,20 +175,26 @@ def time_graph(wl, steps):
 
 
 def kernel_durations(wl, steps):
-    """Average duration of each sampler call from HIP events recorded around
-    it on its launch stream.  The stream is first held by a sleep kernel so
-    the host enqueues ahead: the events then bracket the kernels themselves,
-    not the host's launch latency."""
+    """Average duration of each sampler call from two HIP events on its launch
+    stream around `steps` back-to-back launches of that call alone (rotating
+    logit copies).  The stream is first held by a sleep kernel so the host
+    enqueues ahead: the events then bracket the kernels and the dispatch gaps
+    between them, not the host's launch latency."""
     torch = wl.torch
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)] for _ in wl.calls]
-    torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(steps * 0.08e-3 * 2.0e9))
-    for i in range(steps):
-        wl.step(i, [(e[i][0], e[i][1]) for e in ev])
-    torch.cuda.synchronize()
-    return [sum(a.elapsed_time(b) for a, b in e) / steps for e in ev]
+    out = []
+    for c in wl.calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(steps * 0.05e-3 * 2.0e9))
+        e0.record()
+        for i in range(steps):
+            c.logits = wl.copies[i % wl.ncopies]
+            c()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
 
 
 def roofline(wl, kern_ms):

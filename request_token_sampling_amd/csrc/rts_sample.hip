@@ -169,9 +169,13 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     bool raw_done = false;
     if (LP) {
         const float2 lms = lane_max_sum<EPT>(v, [&]() {
+            // ids below V among the lane's groups of four
             int c = 0;
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) c += ((int)elem_index<EPT>(base, e) < V) ? 1 : 0;
+            for (int q = 0; q < NQ; ++q) {
+                const int left = V - (base + q * 1024 + tid * 4);
+                c += left < 0 ? 0 : (left > 4 ? 4 : left);
+            }
             return c;
         });
         const float2 ms = block_max_sum(sm.s, lms.x, lms.y);
