@@ -126,25 +126,17 @@ int oracle_penalised_row(const float *x, int64_t V, const oracle_row_params *p,
     return 0;
 }
 
-int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
-                      const int32_t *hist, int64_t hlen,
-                      int32_t *token, int32_t counts[3],
-                      int32_t kept_ids[64], float kept_logits[64],
-                      uint32_t *x0, double *u, int32_t *flags)
+/* The chain after the penalties, over a domain of nd candidates already in
+ * the selection order (s sorted by logit desc, index asc). */
+static void chain_on_sorted(const scored *s, int64_t nd, const oracle_row_params *p,
+                            int32_t *token, int32_t counts[3],
+                            int32_t kept_ids[64], float kept_logits[64],
+                            uint32_t *x0, double *u, int32_t *flags)
 {
-    if (V <= 0) return -1;
-    const int greedy = !(p->temperature > 0.0f);       /* NaN refused by callers */
-    if (!greedy && (p->top_k < 1 || p->top_k > 64)) return -1;
-
-    float *y = (float *)malloc((size_t)V * sizeof(float));
-    scored *s = (scored *)malloc((size_t)V * sizeof(scored));
-    if (!y || !s) { free(y); free(s); return -1; }
-    if (oracle_penalised_row(x, V, p, hist, hlen, y) != 0) { free(y); free(s); return -1; }
-
-    /* top_k: the first k_eff of all V under the total order above (R4). */
-    for (int64_t i = 0; i < V; ++i) { s[i].y = y[i]; s[i].i = (int32_t)i; }
-    qsort(s, (size_t)V, sizeof(scored), by_logit_then_index);
-    const int k_eff = greedy ? 1 : (int)((int64_t)p->top_k < V ? p->top_k : V);
+    const int greedy = !(p->temperature > 0.0f);
+    /* top_k: the first k_eff of the domain under the total order (R4) */
+    const int64_t kk = greedy ? 1 : p->top_k;
+    const int k_eff = (int)(kk < nd ? kk : nd);
 
     for (int i = 0; i < 64; ++i) { kept_ids[i] = -1; kept_logits[i] = -INFINITY; }
     for (int i = 0; i < k_eff; ++i) { kept_ids[i] = s[i].i; kept_logits[i] = s[i].y; }
@@ -152,11 +144,24 @@ int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
     *x0 = 0;
     *u = 0.0;
 
+    if (!greedy) {
+        /* the row's draw word (R6); taken even when the domain is empty */
+        const uint32_t ctr[4] = {(uint32_t)p->counter, (uint32_t)(p->counter >> 32), 0u, 0u};
+        const uint32_t key[2] = {(uint32_t)p->seed, (uint32_t)(p->seed >> 32)};
+        uint32_t out[4];
+        oracle_philox4x32_10(ctr, key, out);
+        *x0 = out[0];
+        *u = (double)out[0] * (1.0 / 4294967296.0);
+    }
+    if (nd == 0) {                                      /* R11: nothing to sample */
+        *token = -1;
+        counts[0] = counts[1] = counts[2] = 0;
+        return;
+    }
     if (greedy) {                                       /* argmax, no draw */
         *token = s[0].i;
         counts[0] = counts[1] = counts[2] = 1;
-        free(y); free(s);
-        return 0;
+        return;
     }
 
     /* min_p [P19 "min_p and the penalties"]: keep the prefix whose logit is
@@ -186,15 +191,8 @@ int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
         if (n < 1) n = 1;
     }
 
-    /* temperature, then the Philox draw (R6). */
-    const uint32_t ctr[4] = {(uint32_t)p->counter, (uint32_t)(p->counter >> 32), 0u, 0u};
-    const uint32_t key[2] = {(uint32_t)p->seed, (uint32_t)(p->seed >> 32)};
-    uint32_t out[4];
-    oracle_philox4x32_10(ctr, key, out);
-    *x0 = out[0];
-    const double ud = (double)out[0] * (1.0 / 4294967296.0);
-    *u = ud;
-
+    /* temperature, then the inverse CDF at u (R6). */
+    const double ud = *u;
     int pick = n - 1;                                   /* cdf_{n-1} = 1 > u */
     if (n > 1) {
         const double T = (double)p->temperature;
@@ -212,7 +210,70 @@ int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
     counts[0] = k_eff;
     counts[1] = m;
     counts[2] = n;
-    free(y); free(s);
+}
+
+int oracle_sample_row_masked(const float *x, int64_t V, const oracle_row_params *p,
+                             const int32_t *hist, int64_t hlen,
+                             const int32_t *allowed, int64_t n_allowed,
+                             int32_t *token, int32_t counts[3],
+                             int32_t kept_ids[64], float kept_logits[64],
+                             uint32_t *x0, double *u, int32_t *flags)
+{
+    if (V <= 0) return -1;
+    const int greedy = !(p->temperature > 0.0f);       /* NaN refused by callers */
+    if (!greedy && (p->top_k < 1 || p->top_k > 64)) return -1;
+
+    float *y = (float *)malloc((size_t)V * sizeof(float));
+    scored *s = (scored *)malloc((size_t)V * sizeof(scored));
+    unsigned char *in_d = (unsigned char *)calloc((size_t)V, 1);
+    if (!y || !s || !in_d) { free(y); free(s); free(in_d); return -1; }
+    if (oracle_penalised_row(x, V, p, hist, hlen, y) != 0) {
+        free(y); free(s); free(in_d);
+        return -1;
+    }
+    /* R11: a non-empty allowed list restricts the candidates to its distinct
+     * in-range ids; an empty list leaves the whole vocabulary. */
+    if (allowed != NULL && n_allowed > 0) {
+        for (int64_t j = 0; j < n_allowed; ++j)
+            if (allowed[j] >= 0 && allowed[j] < V) in_d[allowed[j]] = 1;
+    } else {
+        memset(in_d, 1, (size_t)V);
+    }
+    int64_t nd = 0;
+    for (int64_t i = 0; i < V; ++i)
+        if (in_d[i]) { s[nd].y = y[i]; s[nd].i = (int32_t)i; ++nd; }
+    qsort(s, (size_t)nd, sizeof(scored), by_logit_then_index);
+    chain_on_sorted(s, nd, p, token, counts, kept_ids, kept_logits, x0, u, flags);
+    free(y); free(s); free(in_d);
+    return 0;
+}
+
+int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
+                      const int32_t *hist, int64_t hlen,
+                      int32_t *token, int32_t counts[3],
+                      int32_t kept_ids[64], float kept_logits[64],
+                      uint32_t *x0, double *u, int32_t *flags)
+{
+    return oracle_sample_row_masked(x, V, p, hist, hlen, NULL, 0, token, counts, kept_ids,
+                                    kept_logits, x0, u, flags);
+}
+
+/* Speculative verify windows [P19 "What changed": the emitted tokens are the
+ * target's own samples; P559 "Not done (yet)": a sampled row is accepted when
+ * its pick equals the draft].  Row j of a window holds the target's sample
+ * after the first j drafts; draft[r] is the proposal that row r's sample is
+ * compared with.  A window emits 1 + the number of leading rows (before its
+ * last) whose sample equals its draft (R12). */
+int oracle_accept_windows(const int32_t *token, int64_t B, int32_t window,
+                          const int32_t *draft, int32_t *accepted)
+{
+    if (window < 1 || B % window != 0) return -1;
+    for (int64_t w = 0; w < B / window; ++w) {
+        const int64_t r0 = w * window;
+        int32_t a = 0;
+        while (a < window - 1 && token[r0 + a] == draft[r0 + a]) ++a;
+        accepted[w] = a + 1;
+    }
     return 0;
 }
 

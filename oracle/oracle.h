@@ -60,6 +60,22 @@ int oracle_sample_row(const float *x, int64_t V, const oracle_row_params *p,
                       int32_t kept_ids[64], float kept_logits[64],
                       uint32_t *x0, double *u, int32_t *flags);
 
+/* The chain with the candidates restricted to the distinct in-range ids of
+ * `allowed` (n_allowed > 0; R11): k_eff = min(top_k, |D|); an empty D gives
+ * token -1 and counts (0, 0, 0).  n_allowed = 0 is oracle_sample_row. */
+int oracle_sample_row_masked(const float *x, int64_t V, const oracle_row_params *p,
+                             const int32_t *hist, int64_t hlen,
+                             const int32_t *allowed, int64_t n_allowed,
+                             int32_t *token, int32_t counts[3],
+                             int32_t kept_ids[64], float kept_logits[64],
+                             uint32_t *x0, double *u, int32_t *flags);
+
+/* Verify windows of `window` consecutive rows (B a multiple of it):
+ * accepted[w] = 1 + the number of leading rows r of window w, before its
+ * last, with token[r] == draft[r] (R12). */
+int oracle_accept_windows(const int32_t *token, int64_t B, int32_t window,
+                          const int32_t *draft, int32_t *accepted);
+
 /* Penalised and sanitised logits of one row (the chain's first two steps). */
 int oracle_penalised_row(const float *x, int64_t V, const oracle_row_params *p,
                          const int32_t *hist, int64_t hlen, float *y);

@@ -68,8 +68,12 @@ def lib():
                                            P, P, P, P, P, P, P]
         L.oracle_token_logprobs_row.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
                                                 ctypes.c_int32, P, ctypes.c_int64, P, P, P]
+        L.oracle_sample_row_masked.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
+                                               P, ctypes.c_int64, P, P, P, P, P, P, P]
+        L.oracle_accept_windows.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
         for f in ("oracle_sample_row", "oracle_penalised_row", "oracle_sample_tokens",
-                  "oracle_token_logprobs_row"):
+                  "oracle_token_logprobs_row", "oracle_sample_row_masked",
+                  "oracle_accept_windows"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -116,10 +120,12 @@ def penalised_row(x, params: dict, hist=None):
     return y
 
 
-def sample_row(x, params: dict, hist=None) -> dict:
-    """The whole chain on one row; returns a dict of every output."""
+def sample_row(x, params: dict, hist=None, allowed=None) -> dict:
+    """The whole chain on one row; returns a dict of every output.  With a
+    non-empty `allowed`, the candidates are its distinct in-range ids."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     h = None if hist is None else np.ascontiguousarray(hist, dtype=np.int32)
+    a = None if allowed is None else np.ascontiguousarray(allowed, dtype=np.int32)
     p = make_params(params)
     tok = np.zeros(1, np.int32)
     counts = np.zeros(3, np.int32)
@@ -128,9 +134,10 @@ def sample_row(x, params: dict, hist=None) -> dict:
     x0 = np.zeros(1, np.uint32)
     u = np.zeros(1, np.float64)
     fl = np.zeros(1, np.int32)
-    rc = lib().oracle_sample_row(_ptr(x), x.size, ctypes.byref(p), _ptr(h),
-                                 0 if h is None else h.size, _ptr(tok), _ptr(counts),
-                                 _ptr(kid), _ptr(klg), _ptr(x0), _ptr(u), _ptr(fl))
+    rc = lib().oracle_sample_row_masked(_ptr(x), x.size, ctypes.byref(p), _ptr(h),
+                                        0 if h is None else h.size, _ptr(a),
+                                        0 if a is None else a.size, _ptr(tok), _ptr(counts),
+                                        _ptr(kid), _ptr(klg), _ptr(x0), _ptr(u), _ptr(fl))
     if rc != 0:
         raise ValueError("oracle_sample_row refused its input")
     return dict(token=int(tok[0]), counts=counts, kept_ids=kid, kept_logits=klg,
@@ -191,3 +198,37 @@ def token_logprobs(logits, tokens, top_n: int, allowed_lists=None) -> dict:
         tid[r] = o["top_ids"]
         tlp[r] = o["top_lp"]
     return dict(token_lp=lp, top_ids=tid, top_lp=tlp)
+
+
+def sample_tokens_masked(logits, params: list, allowed_lists, history=None,
+                         hist_len=None) -> dict:
+    """B rows, each restricted to its allowed list (None or empty: no
+    restriction); same outputs as sample_tokens."""
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    B, V = x.shape
+    outs = []
+    for r in range(B):
+        h = None
+        p = params[r]
+        if history is not None and p.get("history_row", -1) >= 0:
+            h = np.asarray(history, np.int32)[p["history_row"]][:int(hist_len[p["history_row"]])]
+        a = allowed_lists[r] if allowed_lists is not None else None
+        outs.append(sample_row(x[r], p, h, a))
+    return dict(token=np.array([o["token"] for o in outs], np.int32),
+                counts=np.stack([o["counts"] for o in outs]),
+                kept_ids=np.stack([o["kept_ids"] for o in outs]),
+                kept_logits=np.stack([o["kept_logits"] for o in outs]),
+                x0=np.array([o["x0"] for o in outs], np.uint32),
+                u=np.array([o["u"] for o in outs], np.float64),
+                flags=np.array([o["flags"] for o in outs], np.int32))
+
+
+def accept_windows(tokens, window: int, drafts) -> np.ndarray:
+    """Tokens emitted per verify window of `window` consecutive rows."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    d = np.ascontiguousarray(drafts, dtype=np.int32)
+    out = np.zeros(t.size // window, np.int32)
+    rc = lib().oracle_accept_windows(_ptr(t), t.size, int(window), _ptr(d), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_accept_windows refused its input")
+    return out
