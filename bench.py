@@ -72,6 +72,7 @@ class Workload:
         self.name = name
         hist = hist_len = None
         lp = None
+        spec = {}
         if name == "single_stream":
             w = W.single_stream()
             x = w["logits"]
@@ -85,8 +86,12 @@ class Workload:
             hist = vw.history.reshape(1, -1)
             hist_len = [hist.shape[1]]
             passes = [("sampled", vw.params(0), 5, 5)]
+            # argmax drafts (a drafter proposing its own greedy pick per row)
+            spec = dict(window=5, draft=torch.from_numpy(
+                np.argmax(x, axis=1).astype(np.int32)).to(dev))
             self.desc = ("verify window: 5 rows, V=248,320, penalties 1.1/0.5/0.5 over a "
-                         "64-id history, top_k 40, min_p 0.05, top_p 0.95, temperature 1")
+                         "64-id history, top_k 40, min_p 0.05, top_p 0.95, temperature 1; "
+                         "acceptance of argmax drafts in the same launch")
         elif name == "batch":
             w = W.batch_slots()
             x, hist, hist_len = w["logits"], w["history"], w["hist_len"]
@@ -118,7 +123,7 @@ class Workload:
             self.calls.append(R.SampleCall(self.copies[0], params, self.hist, hist_len,
                                            workspace=self.ws, counters=ctr,
                                            counter_stride=stride,
-                                           logprobs=None if lp is None else lp[0]))
+                                           logprobs=None if lp is None else lp[0], **spec))
             self.labels.append(label)
             self.sampled_rows += counted
         self.lp_calls = []

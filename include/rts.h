@@ -89,6 +89,39 @@ typedef struct rts_logprob_request {
     float *top_lp;
 } rts_logprob_request;
 
+/*
+ * Speculative verify windows and masked sampling for rts_sample_tokens.
+ *   window      rows per verify window (1..64), 0 for none; B must be a
+ *               multiple of it.  Rows r0 .. r0+window-1 hold the target's
+ *               logits after 0, 1, ... drafts of one sequence (#19, "What
+ *               changed": the emitted tokens are the target's own samples;
+ *               #559, "Not done (yet)": a sampled row is accepted when its
+ *               pick equals the draft).
+ *   reserved    must be 0.
+ *   draft       device int32 [B] when window > 0: draft[r] is the proposal
+ *               row r's sample is compared with (ignored on each window's
+ *               last row).
+ *   accepted    device int32 [B / window] when window > 0: the number of
+ *               target tokens the window emits, 1 + the number of leading
+ *               rows whose sample equals their draft.
+ *   allowed     device int32 ids, row r owning allowed[allowed_off[r] ..
+ *               allowed_off[r+1]), or NULL.  A row with a non-empty range
+ *               samples only among its distinct ids in [0, V) (the sampler
+ *               masked by allowed_token_ids): k_eff = min(top_k, that count),
+ *               and with none in range the row's token is -1 and its counts
+ *               are 0.  The fused logprobs stay unrestricted.
+ *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] >= 0,
+ *               allowed_off[B] < 2^31.
+ */
+typedef struct rts_sample_extras {
+    int32_t window;
+    int32_t reserved;
+    const int32_t *draft;
+    int32_t *accepted;
+    const int32_t *allowed;
+    const int64_t *allowed_off;
+} rts_sample_extras;
+
 /* Bytes of workspace that calls with up to B rows of V logits need
  * (both entry points).  *bytes is set on RTS_OK. */
 int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes);
@@ -124,12 +157,17 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
  *               "#19 ...", "Problem": a captured sampler would replay the same
  *               draws forever; "A persistent per-request draw counter").
  *   lp          host, or NULL for no logprobs: see rts_logprob_request.
+ *   ex          host, or NULL: verify windows and allowed-id masks, see
+ *               rts_sample_extras.
  * Errors: RTS_EINVAL for B < 0, V out of range, ld < V, NULL logits/token,
  * a row with NaN or infinite temperature, top_k outside 1..64 on a sampled
  * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
  * non-finite penalties, history_row >= H or set without history, a window
- * longer than RTS_MAX_WINDOW, reserved != 0, or an lp request with top_n
- * outside 0..20, reserved != 0 or a NULL output it needs; RTS_ENOSPC for a short
+ * longer than RTS_MAX_WINDOW, reserved != 0, an lp request with top_n
+ * outside 0..20, reserved != 0 or a NULL output it needs, extras with a
+ * window outside 0..64 or not dividing B, missing draft / accepted, or bad
+ * allowed offsets, or history offsets (history_row * ldh + length) of 2^31
+ * or more; RTS_ENOSPC for a short
  * workspace; RTS_EDEVICE if a launch fails.  B = 0 is a no-op.
  */
 int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
@@ -139,7 +177,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
                       uint64_t *counters, int64_t counter_stride,
-                      const rts_logprob_request *lp,
+                      const rts_logprob_request *lp, const rts_sample_extras *ex,
                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -65,6 +65,22 @@ class LogprobRequest(ctypes.Structure):
 
 assert ctypes.sizeof(LogprobRequest) == 32
 
+
+class SampleExtras(ctypes.Structure):
+    """Mirror of rts_sample_extras: verify windows with drafts, and allowed-id
+    lists that restrict a row's candidates."""
+    _fields_ = [
+        ("window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("draft", ctypes.c_void_p),
+        ("accepted", ctypes.c_void_p),
+        ("allowed", ctypes.c_void_p),
+        ("allowed_off", ctypes.c_void_p),
+    ]
+
+
+assert ctypes.sizeof(SampleExtras) == 40
+
 _DEFAULTS = dict(temperature=0.0, top_k=0, top_p=1.0, min_p=0.0, penalty_repeat=1.0,
                  penalty_freq=0.0, penalty_present=0.0, penalty_last_n=0, history_row=-1,
                  reserved=0, seed=0, counter=0)
@@ -84,7 +100,7 @@ def lib() -> ctypes.CDLL:
         L.rts_workspace_bytes.argtypes = [I64, I64, ctypes.POINTER(ctypes.c_size_t)]
         L.rts_workspace_init.argtypes = [P, SZ, P]
         L.rts_sample_tokens.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P, P, P,
-                                        I64, P, P, SZ, P]
+                                        I64, P, P, P, SZ, P]
         L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
         L.rts_read_rows.argtypes = [P, I64, I64, I64, P, P]
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
@@ -153,7 +169,8 @@ class SampleCall:
     with ``set_params``."""
 
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
-                 stream=None, counters=None, counter_stride=0, logprobs=None):
+                 stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
+                 draft=None, allowed=None, allowed_off=None):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -185,6 +202,24 @@ class SampleCall:
             self.lp = LogprobRequest(n, 0, self.token_lp.data_ptr(),
                                      self.top_ids.data_ptr() if n > 0 else None,
                                      self.top_lp.data_ptr() if n > 0 else None)
+        # verify windows (window rows each, drafts per row) and allowed-id masks
+        self.ex = None
+        self.accepted = None
+        if window or allowed is not None:
+            if window:
+                if draft is None or draft.dtype != torch.int32 or not draft.is_cuda:
+                    raise ValueError("window needs draft: a CUDA int32 tensor of B ids")
+                self.accepted = torch.empty(max(self.B // int(window), 1), dtype=torch.int32,
+                                            device=dev)
+            self.draft = draft
+            self.allowed = allowed
+            self.allowed_off = (None if allowed is None
+                                else np.ascontiguousarray(allowed_off, dtype=np.int64))
+            self.ex = SampleExtras(int(window), 0, None if draft is None else draft.data_ptr(),
+                                   None if self.accepted is None else self.accepted.data_ptr(),
+                                   None if allowed is None else allowed.data_ptr(),
+                                   None if allowed is None
+                                   else self.allowed_off.ctypes.data_as(ctypes.c_void_p))
         self.set_params(params)
         self.stream = stream
 
@@ -200,6 +235,7 @@ class SampleCall:
             _ptr(self.token), _ptr(self.counts), _ptr(self.kept_ids), _ptr(self.kept_logits),
             _ptr(self.philox_x0), _ptr(self.counters), self.counter_stride,
             None if self.lp is None else ctypes.byref(self.lp),
+            None if self.ex is None else ctypes.byref(self.ex),
             _ptr(self.workspace), self.workspace.numel(), None]
 
     def __call__(self):
@@ -207,7 +243,7 @@ class SampleCall:
             self._build_args()
         a = self._args
         a[0] = self.logits.data_ptr()
-        a[19] = _stream_handle(self.stream)
+        a[20] = _stream_handle(self.stream)
         _check(lib().rts_sample_tokens(*a))
         return self
 
@@ -217,11 +253,14 @@ class SampleCall:
                  kept_logits=self.kept_logits, philox_x0=self.philox_x0)
         if self.lp is not None:
             r.update(token_lp=self.token_lp, top_ids=self.top_ids, top_lp=self.top_lp)
+        if self.accepted is not None:
+            r.update(accepted=self.accepted)
         return r
 
 
 def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
-                  stream=None, counters=None, counter_stride=0, logprobs=None) -> dict:
+                  stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
+                  draft=None, allowed=None, allowed_off=None) -> dict:
     """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
 
     params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
@@ -231,9 +270,13 @@ def sample_tokens(logits, params, history=None, history_len=None, workspace=None
     device-resident Philox counters, advanced by counter_stride per call.
     logprobs: None, or top_n in 0..20 to add token_lp[B], top_ids[B][top_n]
     and top_lp[B][top_n], the raw-logit logprobs of the sampled tokens,
-    computed in the same pass over the logits."""
+    computed in the same pass over the logits.
+    window, draft: verify windows of `window` rows with a CUDA int32 draft id
+    per row; adds accepted[B / window], the tokens each window emits.
+    allowed, allowed_off: CUDA int32 ids with host int64 offsets [B+1]; a row
+    with a non-empty list samples only among those ids."""
     return SampleCall(logits, params, history, history_len, workspace, stream, counters,
-                      counter_stride, logprobs)().results()
+                      counter_stride, logprobs, window, draft, allowed, allowed_off)().results()
 
 
 class LogprobCall:
@@ -302,5 +345,6 @@ class ReadCall:
 
 
 __all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
-           "make_workspace", "row_params", "RowParams", "LogprobRequest", "ReadCall", "RTSError",
+           "make_workspace", "row_params", "RowParams", "LogprobRequest", "SampleExtras", "ReadCall",
+           "RTSError",
            "lib"]

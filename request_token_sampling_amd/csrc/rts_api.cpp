@@ -113,7 +113,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       int32_t *token, int32_t *counts, int32_t *kept_ids,
                       float *kept_logits, uint32_t *philox_x0,
                       uint64_t *counters, int64_t counter_stride,
-                      const rts_logprob_request *lp,
+                      const rts_logprob_request *lp, const rts_sample_extras *ex,
                       void *workspace, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
@@ -134,6 +134,28 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         if (lp->token_lp == nullptr) return fail(RTS_EINVAL, "lp->token_lp is NULL");
         if (lp->top_n > 0 && (lp->top_ids == nullptr || lp->top_lp == nullptr))
             return fail(RTS_EINVAL, "lp->top_ids / lp->top_lp are NULL with top_n = %d", lp->top_n);
+    }
+    const int window = ex ? ex->window : 0;
+    const int32_t *allowed = ex ? ex->allowed : nullptr;
+    const int64_t *allowed_off = ex ? ex->allowed_off : nullptr;
+    if (ex != nullptr) {
+        if (ex->reserved != 0) return fail(RTS_EINVAL, "ex->reserved is not 0");
+        if (window < 0 || window > rts::kRowsPerLaunch)
+            return fail(RTS_EINVAL, "ex->window = %d outside 0..64", window);
+        if (window > 0 && B % window != 0)
+            return fail(RTS_EINVAL, "B = %lld is not a multiple of ex->window = %d", (long long)B,
+                        window);
+        if (window > 0 && (ex->draft == nullptr || ex->accepted == nullptr))
+            return fail(RTS_EINVAL, "ex->draft / ex->accepted are NULL with window = %d", window);
+        if (allowed != nullptr) {
+            if (allowed_off == nullptr) return fail(RTS_EINVAL, "ex->allowed without allowed_off");
+            if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");
+            for (int64_t r = 0; r < B; ++r)
+                if (allowed_off[r + 1] < allowed_off[r])
+                    return fail(RTS_EINVAL, "allowed_off decreases at row %lld", (long long)r);
+            if (allowed_off[B] > 0x7FFFFFFFLL)
+                return fail(RTS_EINVAL, "allowed_off[B] = %lld >= 2^31", (long long)allowed_off[B]);
+        }
     }
     size_t need = 0;
     rts_workspace_bytes(B, V, &need);
@@ -173,6 +195,8 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             if (hl < 0 || hl > ldh)
                 return fail(RTS_EINVAL, "history row %d: length %d outside [0, ldh = %lld]",
                             p.history_row, hl, (long long)ldh);
+            if ((int64_t)p.history_row * ldh + hl > 0x7FFFFFFFLL)
+                return fail(RTS_EINVAL, "row %lld: history offset of 2^31 ids or more", rr);
             const int64_t n_eff = p.penalty_last_n < 0 ? hl
                                   : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
             if (n_eff > RTS_MAX_WINDOW)
@@ -183,8 +207,11 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
 
     char *ws = static_cast<char *>(workspace);
     const rts::WsLayout L = rts::ws_layout(B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch, V);
-    for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
-        const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
+    // A launch covers whole verify windows.
+    const int64_t per_launch = window > 0 ? (rts::kRowsPerLaunch / window) * window
+                                          : rts::kRowsPerLaunch;
+    for (int64_t r0 = 0; r0 < B; r0 += per_launch) {
+        const int rows = (int)((B - r0) < per_launch ? (B - r0) : per_launch);
         const int ept = choose_ept(rows, V);
         rts::SampleArgs a;
         std::memset(&a, 0, sizeof a);
@@ -205,6 +232,13 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
         a.rows = rows;
         a.early_xcds = rows * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
+        a.allowed = allowed;
+        if (window > 0) {
+            a.window = window;
+            a.draft = ex->draft + r0;
+            a.accepted = ex->accepted + r0 / window;
+            a.wtickets = reinterpret_cast<uint32_t *>(ws + 2 * rts::kTicketRegion);
+        }
         if (lp != nullptr) {
             a.lp_on = 1;
             a.lp_topn = lp->top_n;
@@ -231,7 +265,9 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             }
             s.seed = p.seed;
             s.counter = p.counter;
-            s.hist_off = hist_off;
+            s.hist_off = (int32_t)hist_off;
+            s.allowed_off = allowed ? (int32_t)allowed_off[r0 + i] : 0;
+            s.allowed_cnt = allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0;
             s.lnp = logf(p.min_p);
             s.top_p = p.top_p;
             s.temperature = p.temperature;

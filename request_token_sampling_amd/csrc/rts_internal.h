@@ -23,11 +23,12 @@ constexpr int kMinWavesPerSimd = 5;
 //                  ticket, and rows sharing a line would queue behind each
 //                  other's atomics
 //   [8192, 16384)  logprob tickets, laid out the same way
+//   [16384, 24576) verify-window tickets, one per window slot of a launch
 //   then, for every row slot of a launch: chunk candidate keys (64 per chunk),
 //   raw-logit top-K keys (20 per chunk) and (max, sum) partials (one per chunk)
 constexpr int kTicketStride = 32;  // uint32 words between two row slots' tickets
 constexpr size_t kTicketRegion = (size_t)kRowsPerLaunch * kTicketStride * 4u;
-constexpr size_t kTicketBytes = 2 * kTicketRegion;
+constexpr size_t kTicketBytes = 3 * kTicketRegion;
 
 // Static LDS of the allowed-ids kernels besides their dynamic bitmap / list.
 constexpr size_t kAllowedStaticLds = 10240;
@@ -61,7 +62,8 @@ inline WsLayout ws_layout(int64_t rows_ws, int64_t V)
 struct SampleRow {
     uint64_t seed;
     uint64_t counter;
-    int64_t hist_off;      // element offset of the window's first id in `history`
+    int32_t hist_off;      // element offset of the window's first id in `history`
+    int32_t allowed_off;   // first id of the row's allowed list in `allowed`
     float lnp;             // logf(min_p); -inf for min_p = 0
     float top_p;
     float temperature;
@@ -69,6 +71,7 @@ struct SampleRow {
     float freq;
     float present;
     uint32_t pack;         // bits 0..15 window length, 16..22 k_eff, 24 greedy
+    int32_t allowed_cnt;   // 0: every id is a candidate
 };
 static_assert(sizeof(SampleRow) == 56, "argument block layout");
 
@@ -100,6 +103,12 @@ struct SampleArgs {
     float *lp_token;       // outputs, row 0 of this launch
     int32_t *lp_ids;
     float *lp_top;
+    const int32_t *allowed;  // candidate lists of masked rows (row[].allowed_off/cnt)
+    const int32_t *draft;    // verify windows: draft id per row, row 0 of this launch
+    int32_t *accepted;       // tokens emitted per window, window 0 of this launch
+    uint32_t *wtickets;      // workspace: one ticket per window slot
+    int32_t window;          // rows per verify window; 0: none
+    int32_t pad3_;
     SampleRow row[kRowsPerLaunch];
 };
 // HIP passes at most 4 KiB of kernel arguments.

@@ -68,6 +68,37 @@ __device__ __forceinline__ void load_chunk(const float *x, int base, int V, floa
     }
 }
 
+// Verify windows (page "#19 ...", "What changed": the emitted tokens are the
+// target's own samples; page "#559 ...", "Not done (yet)": a sampled row is
+// accepted when its pick equals the draft).  Run by wave 0 of a row's merging
+// workgroup once the row's token is published: the window's last row to get
+// here counts the leading rows whose token equals their draft and writes the
+// number of tokens the window emits.
+__device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32_t tok)
+{
+    const int lane = lane_id();
+    const int w = slot / a.window;
+    uint32_t last = 0u;
+    if (lane == 0) {
+        wait_stores_complete();
+        const uint32_t old = __hip_atomic_fetch_add(&a.wtickets[w * kTicketStride], 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old == (uint32_t)a.window - 1u) ? 1u : 0u;
+    }
+    if (lane_u32(last, 0) == 0u) return;
+    const int r0 = w * a.window;
+    bool miss = false;
+    if (lane < a.window - 1) {
+        const int32_t t = (r0 + lane == slot) ? tok : read_published_i32(&a.token[r0 + lane]);
+        miss = t != a.draft[r0 + lane];
+    }
+    const uint64_t b = __ballot(miss);
+    if (lane == 0) {
+        a.accepted[w] = b ? __ffsll((unsigned long long)b) : a.window;
+        a.wtickets[w * kTicketStride] = 0u;
+    }
+}
+
 // The cuts and the draw, run by wave 0 of the row's last workgroup on the
 // merged kept sequence sm.sel[0..k).  Leaves the sampled token in sm.flag.
 __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
@@ -80,10 +111,13 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     const float y = valid ? key_logit(key) : -INFINITY;
     if (a.kept_ids) a.kept_ids[(int64_t)slot * kMaxK + lane] = id;
     if (a.kept_logits) a.kept_logits[(int64_t)slot * kMaxK + lane] = y;
+    // The kept sequence holds k keys, or fewer when a row's allowed ids are
+    // fewer than k (zero keys sort last); an empty one samples nothing.
+    k = __popcll(__ballot(valid));
 
     const float y0 = lane_f32(y, 0);
-    int m = 1, n = 1, pick = 0;
-    if (!greedy) {
+    int m = k > 0 ? 1 : 0, n = m, pick = 0;
+    if (!greedy && k > 0) {
         // Everything that does not depend on the cuts first: top_p weights
         // exp(y - y0) and tempered weights exp((y - y0) / T).
         const double dy = (double)y - (double)y0;
@@ -118,7 +152,8 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     const int32_t tok = lane_i32(id, pick);
     if (lane == 0) {
         sm.flag = (uint32_t)tok;
-        a.token[slot] = tok;
+        if (a.window > 0) publish_i32(&a.token[slot], tok);  // read by the window's last row
+        else a.token[slot] = tok;
         if (a.counts) {
             a.counts[3 * (int64_t)slot + 0] = k;
             a.counts[3 * (int64_t)slot + 1] = m;
@@ -128,6 +163,7 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
         if (a.counters) a.counters[slot] = ctr + (uint64_t)a.counter_stride;
         a.tickets[slot * kTicketStride] = 0u;  // ready for the next launch on this workspace
     }
+    if (a.window > 0) window_step(a, slot, tok);
 }
 
 template <int EPT, bool VEC, bool LP>
@@ -163,7 +199,8 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // ranked after the penalised selection, so only one set of values is
     // held in registers at a time.
     const int K = LP ? a.lp_topn : 0;
-    const bool raw_sel = LP && K > 0 && !(n_eff == 0 && k >= K);
+    const bool masked = R.allowed_cnt > 0;
+    const bool raw_sel = LP && K > 0 && !(n_eff == 0 && !masked && k >= K);
     const Cands rawc{sm.raw_keys, sm.raw_cnt};
     uint64_t *raw_out = LP ? a.raw_keys + (int64_t)slot * a.raw_stride + (int64_t)chunk * K : nullptr;
     bool raw_done = false;
@@ -221,8 +258,34 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         }
     }
 
+    // A row with an allowed list samples among those ids only: the chunk's
+    // members are marked in LDS (in the penalty bitmap's space, free by now)
+    // and every other id reads as absent (NaN); members are sanitised, so a
+    // NaN member still counts as -inf.
+    if (masked) {
+        __syncthreads();  // penalty lookups may still read the bitmap
+        for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
+        __syncthreads();
+        const int32_t *al = a.allowed + R.allowed_off;
+        for (int j = tid; j < R.allowed_cnt; j += kBlock) {
+            const int32_t id = al[j];
+            const int rel = id - base;
+            if (id >= 0 && id < V && rel >= 0 && rel < CH)
+                atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int rel = q * 1024 + tid * 4;
+            const uint32_t nib = (sm.pen_bits[rel >> 5] >> (rel & 31)) & 0xFu;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                v[4 * q + s] = ((nib >> s) & 1u) ? sanitize(v[4 * q + s]) : __builtin_nanf("");
+        }
+    }
+
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k);
+    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k, masked);
 
     if (raw_sel && !raw_done) {
         __syncthreads();  // the penalised selection's rank may still read sm.part

@@ -172,10 +172,12 @@ __device__ __forceinline__ uint32_t elem_index(int base, int e)
 // into cd, whose regions are padded; ends after a barrier.  For k = 1 the
 // argmax is written to out[0] directly and true is returned (nothing left to
 // do); otherwise returns false.  In the degenerate case (fewer than k values
-// above -inf) every id below V is a candidate and v is sanitised in place.
+// above -inf) every id below V is a candidate and v is sanitised in place;
+// with nan_absent, a NaN marks an id outside the row's candidate set (the
+// caller has sanitised the others) and stays excluded.
 template <int EPT, typename Out>
 __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], int base, int V,
-                                              int k, Cands cd, Out out)
+                                              int k, Cands cd, Out out, bool nan_absent = false)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     constexpr float kFltMax = 3.40282346638528859812e+38f;
@@ -221,10 +223,11 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
     const float tf = key_threshold(sm.thr);
     if (tf == -INFINITY) {
         // Degenerate chunk (fewer than k values above -inf): every id below V
-        // is a candidate, NaN counting as -inf.
+        // is a candidate, NaN counting as -inf (unless it marks an absent id).
 #pragma unroll
         for (int e = 0; e < EPT; ++e)
-            v[e] = ((int)elem_index<EPT>(base, e) < V) ? sanitize(v[e]) : __builtin_nanf("");
+            v[e] = ((int)elem_index<EPT>(base, e) < V && (!nan_absent || v[e] == v[e]))
+                       ? sanitize(v[e]) : __builtin_nanf("");
     }
 
     // Ballot compaction of the raw entries (float bits, id): the slot is the
@@ -274,7 +277,7 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
 // barrier must separate it from the tail of an earlier rank.
 template <int EPT, typename Out>
 __device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EPT], int base, int V,
-                                             int k, Cands cd, Out out)
+                                             int k, Cands cd, Out out, bool nan_absent = false)
 {
     const int tid = threadIdx.x;
     if (!any_overflow(cd)) {
@@ -296,7 +299,7 @@ __device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EP
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const uint32_t idx = elem_index<EPT>(base, e);
-            if ((int)idx < V) {
+            if ((int)idx < V && (!nan_absent || v[e] == v[e])) {
                 const uint64_t key = cand_key(sanitize(v[e]), idx);
                 best = (key < prev && key > best) ? key : best;
             }
@@ -314,11 +317,11 @@ __device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EP
 // out_keys[0..k) with device-coherent stores.  Ends without a barrier.
 template <int EPT>
 __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int base, int V, int k,
-                                           uint64_t *out_keys)
+                                           uint64_t *out_keys, bool nan_absent = false)
 {
     const ToWorkspace out{out_keys};
-    if (chunk_compact<EPT>(sm, v, base, V, k, own_cands(sm), out)) return;
-    chunk_finish<EPT>(sm, v, base, V, k, own_cands(sm), out);
+    if (chunk_compact<EPT>(sm, v, base, V, k, own_cands(sm), out, nan_absent)) return;
+    chunk_finish<EPT>(sm, v, base, V, k, own_cands(sm), out, nan_absent);
 }
 
 // Row merge: top-k of the chunk lists, written in order to sm.sel[0..k).

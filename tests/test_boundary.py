@@ -51,7 +51,7 @@ def test_struct_layout_matches_header():
 
 
 def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws_bytes=BIG_WS,
-           history=None, H=0, ldh=0, hist_len=None, lp=None):
+           history=None, H=0, ldh=0, hist_len=None, lp=None, ex=None):
     L = R.lib()
     arr = R.row_params(params)
     B = len(params) if B is None else B
@@ -60,7 +60,8 @@ def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws
         hl = (ctypes.c_int32 * len(hist_len))(*hist_len)
     return L.rts_sample_tokens(logits, B, V, V if ld is None else ld, arr, history, H, ldh, hl,
                                token, None, None, None, None, None, 0,
-                               None if lp is None else ctypes.byref(lp), ws, ws_bytes, None)
+                               None if lp is None else ctypes.byref(lp),
+                               None if ex is None else ctypes.byref(ex), ws, ws_bytes, None)
 
 
 SAMPLED = dict(temperature=0.7, top_k=20, top_p=0.9, min_p=0.05, seed=1, counter=0)
@@ -139,6 +140,46 @@ def test_logprob_request_without_top_entries_needs_no_top_buffers():
     lp = R.LogprobRequest(top_n=0, reserved=0, token_lp=4096, top_ids=None, top_lp=None)
     assert sample([dict(SAMPLED, top_k=0)], lp=lp) == R.RTS_EINVAL
     assert "top_k" in last_error()
+
+
+def extras(**kw):
+    d = dict(window=0, reserved=0, draft=None, accepted=None, allowed=None, allowed_off=None)
+    d.update(kw)
+    return R.SampleExtras(**d)
+
+
+def test_bad_extras_are_refused():
+    rows = [dict(SAMPLED) for _ in range(10)]
+    off_ok = (ctypes.c_int64 * 11)(*range(11))
+    off_down = (ctypes.c_int64 * 11)(*([0, 5] + [3] * 9))
+    off_neg = (ctypes.c_int64 * 11)(*([-1] + list(range(10))))
+    off_big = (ctypes.c_int64 * 11)(*([0] * 10 + [2 ** 31]))
+    cases = [
+        (extras(reserved=1), "reserved"),
+        (extras(window=65, draft=4096, accepted=4096), "window"),
+        (extras(window=-1), "window"),
+        (extras(window=3, draft=4096, accepted=4096), "multiple"),
+        (extras(window=5, accepted=4096), "draft"),
+        (extras(window=5, draft=4096), "accepted"),
+        (extras(allowed=4096), "allowed_off"),
+        (extras(allowed=4096, allowed_off=ctypes.cast(off_down, ctypes.c_void_p)), "decreases"),
+        (extras(allowed=4096, allowed_off=ctypes.cast(off_neg, ctypes.c_void_p)), "allowed_off[0]"),
+        (extras(allowed=4096, allowed_off=ctypes.cast(off_big, ctypes.c_void_p)), "2^31"),
+    ]
+    for ex, word in cases:
+        assert sample(rows, ex=ex) == R.RTS_EINVAL, word
+        assert word in last_error(), (word, last_error())
+    # a valid window and list pass validation: the bad row then names itself
+    bad = [dict(SAMPLED) for _ in range(9)] + [dict(SAMPLED, top_k=0)]
+    ex = extras(window=5, draft=4096, accepted=4096, allowed=4096,
+                allowed_off=ctypes.cast(off_ok, ctypes.c_void_p))
+    assert sample(bad, ex=ex) == R.RTS_EINVAL and "row 9" in last_error()
+
+
+def test_history_offsets_beyond_int32_are_refused():
+    rows = [dict(SAMPLED, history_row=2, penalty_last_n=-1, penalty_repeat=1.1)]
+    assert sample(rows, history=FAKE, H=3, ldh=2 ** 30, hist_len=[0, 0, 5]) == R.RTS_EINVAL
+    assert "2^31" in last_error()
 
 
 def test_short_workspace():
