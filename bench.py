@@ -114,6 +114,8 @@ class Workload:
         base = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
         self.copies = base.unsqueeze(0).repeat(self.ncopies, 1, 1)
         self.hist = None if hist is None else torch.from_numpy(np.asarray(hist, np.int32)).to(dev)
+        self.hist_len = hist_len
+        self.first_params = passes[0][1]
         self.ws = R.make_workspace(self.B, self.V, dev)
         self.calls, self.labels = [], []
         self.sampled_rows = 0
@@ -245,6 +247,53 @@ def read_floor(wl, launches=400):
     gbs = wl.B * wl.row_bytes / (us * 1e-6) / 1e9
     return dict(kernel="rts::read_rows_kernel", us_per_launch=round(us, 3), achieved=round(gbs, 1),
                 frac=round(gbs / HBM_PEAK_GBS, 4))
+
+
+def per_launch_us(wl, call, launches):
+    """Average time of `launches` back-to-back launches of one prepared call
+    over rotating copies, between two events with the host enqueued ahead."""
+    torch = wl.torch
+    call.logits = wl.copies[0]
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(launches * 0.05e-3 * 2.0e9))
+    e0.record()
+    for i in range(launches):
+        call.logits = wl.copies[i % wl.ncopies]
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / launches * 1e3, 2)
+
+
+def ablations(dev):
+    """The pages' earlier designs (one thread per row with k rescans; one
+    workgroup per row with k argmax rounds and a penalty bitmap; the same with
+    the per-candidate recount) against the single-pass kernel, same outputs,
+    microseconds per launch."""
+    import request_token_sampling_amd as R
+    out = {}
+    for name, launches in (("single_stream", 8), ("window", 4)):
+        wl = Workload(name, dev)
+        params = wl.first_params
+        ws = R.make_workspace(wl.B, wl.V, dev)
+        single = R.SampleCall(wl.copies[0], params, wl.hist, wl.hist_len, workspace=ws)
+        res = {"single_pass_us": per_launch_us(wl, single, 300)}
+        for label, design, n in (("prior_block_us", R.PRIOR_BLOCK, 4 * launches),
+                                 ("prior_recount_us", R.PRIOR_RECOUNT, launches),
+                                 ("prior_thread_us", R.PRIOR_THREAD, launches)):
+            call = R.PriorCall(design, wl.copies[0], params, wl.hist, wl.hist_len, workspace=ws)
+            res[label] = per_launch_us(wl, call, n)
+            progress(f"ablation {name}: {label} {res[label]} us")
+        res["rows"] = wl.B
+        out[name] = res
+        del wl
+        wl = None
+        import torch
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure(wl, steps, warmup):
@@ -467,6 +516,8 @@ def main():
             del w2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
+    if not args.no_extra:
+        line["ablations"] = ablations(dev)
     if not args.no_cpu_baseline:
         progress(f"oracle on the host for about {args.cpu_seconds} s")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -22,6 +22,7 @@ RTS_OK, RTS_EINVAL, RTS_ENOSPC, RTS_EDEVICE = 0, -1, -2, -3
 MAX_TOP_K = 64
 KEPT = 64
 MAX_TOP_N = 20
+PRIOR_THREAD, PRIOR_BLOCK, PRIOR_RECOUNT = 1, 2, 3
 
 
 class RTSError(RuntimeError):
@@ -103,8 +104,10 @@ def lib() -> ctypes.CDLL:
                                         I64, P, P, P, SZ, P]
         L.rts_token_logprobs.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, P, P, SZ, P]
         L.rts_read_rows.argtypes = [P, I64, I64, I64, P, P]
+        L.rts_sample_tokens_prior.argtypes = [I32, P, I64, I64, I64, P, P, I64, I64, P, P, P, P,
+                                              P, P, P, SZ, P]
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
-                  "rts_token_logprobs", "rts_read_rows"):
+                  "rts_token_logprobs", "rts_read_rows", "rts_sample_tokens_prior"):
             getattr(L, f).restype = ctypes.c_int
         L.rts_strerror.argtypes = [ctypes.c_int]
         L.rts_strerror.restype = ctypes.c_char_p
@@ -328,6 +331,26 @@ def token_logprobs(logits, tokens, top_n: int, allowed=None, allowed_off=None,
                        stream)().results()
 
 
+class PriorCall(SampleCall):
+    """One prepared call of rts_sample_tokens_prior: the pages' earlier designs
+    (PRIOR_THREAD, PRIOR_BLOCK, PRIOR_RECOUNT) over the same arguments, with
+    the same outputs as SampleCall, for measurement against it."""
+
+    def __init__(self, design, logits, params, history=None, history_len=None, workspace=None,
+                 stream=None):
+        super().__init__(logits, params, history, history_len, workspace, stream)
+        self.design = int(design)
+
+    def __call__(self):
+        hl = None if self.hist_len is None else self.hist_len.ctypes.data_as(ctypes.c_void_p)
+        _check(lib().rts_sample_tokens_prior(
+            self.design, self.logits.data_ptr(), self.B, self.V, self.ld, self.params,
+            _ptr(self.history), self.H, self.ldh, hl, _ptr(self.token), _ptr(self.counts),
+            _ptr(self.kept_ids), _ptr(self.kept_logits), _ptr(self.philox_x0),
+            _ptr(self.workspace), self.workspace.numel(), _stream_handle(self.stream)))
+        return self
+
+
 class ReadCall:
     """One prepared call of rts_read_rows, the plain streaming read of the
     rows used as the sampler's bandwidth measuring stick."""
@@ -346,5 +369,6 @@ class ReadCall:
 
 __all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
            "make_workspace", "row_params", "RowParams", "LogprobRequest", "SampleExtras", "ReadCall",
+           "PriorCall",
            "RTSError",
            "lib"]

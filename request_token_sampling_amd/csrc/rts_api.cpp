@@ -14,6 +14,10 @@
 
 #include "rts_internal.h"
 
+static_assert(rts::PRIOR_THREAD == RTS_PRIOR_THREAD && rts::PRIOR_BLOCK == RTS_PRIOR_BLOCK &&
+                  rts::PRIOR_RECOUNT == RTS_PRIOR_RECOUNT,
+              "design numbers of the C ABI and the kernels");
+
 namespace {
 
 thread_local char g_last_error[512];
@@ -65,6 +69,84 @@ size_t max_lds_per_block()
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return 65536;
     return (size_t)v;
+}
+
+// Every row's parameters (and its history window), before anything is
+// enqueued; returns RTS_OK or the error of the first bad row.
+int check_rows(int64_t B, const rts_row_params *params, const int32_t *history, int64_t H,
+               int64_t ldh, const int32_t *history_len)
+{
+    for (int64_t r = 0; r < B; ++r) {
+        const rts_row_params &p = params[r];
+        const long long rr = (long long)r;
+        if (std::isnan(p.temperature) || std::isinf(p.temperature))
+            return fail(RTS_EINVAL, "row %lld: temperature is not finite", rr);
+        const bool greedy = !(p.temperature > 0.0f);
+        if (!greedy && (p.top_k < 1 || p.top_k > RTS_MAX_TOP_K))
+            return fail(RTS_EINVAL, "row %lld: top_k = %d outside 1..64 on a sampled row", rr, p.top_k);
+        if (!(p.top_p > 0.0f && p.top_p <= 1.0f))
+            return fail(RTS_EINVAL, "row %lld: top_p = %g outside (0, 1]", rr, (double)p.top_p);
+        if (!(p.min_p >= 0.0f && p.min_p <= 1.0f))
+            return fail(RTS_EINVAL, "row %lld: min_p = %g outside [0, 1]", rr, (double)p.min_p);
+        if (!(p.penalty_repeat > 0.0f) || std::isinf(p.penalty_repeat))
+            return fail(RTS_EINVAL, "row %lld: penalty_repeat = %g must be finite > 0", rr,
+                        (double)p.penalty_repeat);
+        if (!std::isfinite(p.penalty_freq) || !std::isfinite(p.penalty_present))
+            return fail(RTS_EINVAL, "row %lld: penalty_freq / penalty_present not finite", rr);
+        if (p.penalty_last_n < -1)
+            return fail(RTS_EINVAL, "row %lld: penalty_last_n = %d < -1", rr, p.penalty_last_n);
+        if (p.history_row < -1)
+            return fail(RTS_EINVAL, "row %lld: history_row = %d < -1", rr, p.history_row);
+        if (p.reserved != 0) return fail(RTS_EINVAL, "row %lld: reserved field is not 0", rr);
+        if (p.history_row >= 0) {
+            if (history == nullptr || history_len == nullptr)
+                return fail(RTS_EINVAL, "row %lld: history_row set without history", rr);
+            if (p.history_row >= H)
+                return fail(RTS_EINVAL, "row %lld: history_row = %d >= H = %lld", rr,
+                            p.history_row, (long long)H);
+            const int32_t hl = history_len[p.history_row];
+            if (hl < 0 || hl > ldh)
+                return fail(RTS_EINVAL, "history row %d: length %d outside [0, ldh = %lld]",
+                            p.history_row, hl, (long long)ldh);
+            if ((int64_t)p.history_row * ldh + hl > 0x7FFFFFFFLL)
+                return fail(RTS_EINVAL, "row %lld: history offset of 2^31 ids or more", rr);
+            const int64_t n_eff = p.penalty_last_n < 0 ? hl
+                                  : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
+            if (n_eff > RTS_MAX_WINDOW)
+                return fail(RTS_EINVAL, "row %lld: penalty window of %lld ids > %d", rr,
+                            (long long)n_eff, RTS_MAX_WINDOW);
+        }
+    }
+
+    return RTS_OK;
+}
+
+// The kernel's view of one checked row.
+void pack_row(rts::SampleRow &s, const rts_row_params &p, int64_t V, const int32_t *history_len,
+              int64_t ldh, int32_t allowed_off, int32_t allowed_cnt)
+{
+    const bool greedy = !(p.temperature > 0.0f);
+    const int64_t k_eff = greedy ? 1 : (p.top_k < V ? p.top_k : V);
+    int64_t n_eff = 0, hist_off = 0;
+    const bool neutral = p.penalty_repeat == 1.0f && p.penalty_freq == 0.0f &&
+                         p.penalty_present == 0.0f;
+    if (p.history_row >= 0 && !neutral) {
+        const int32_t hl = history_len[p.history_row];
+        n_eff = p.penalty_last_n < 0 ? hl : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
+        hist_off = (int64_t)p.history_row * ldh + (hl - n_eff);
+    }
+    s.seed = p.seed;
+    s.counter = p.counter;
+    s.hist_off = (int32_t)hist_off;
+    s.allowed_off = allowed_off;
+    s.allowed_cnt = allowed_cnt;
+    s.lnp = logf(p.min_p);
+    s.top_p = p.top_p;
+    s.temperature = p.temperature;
+    s.rep = p.penalty_repeat;
+    s.freq = p.penalty_freq;
+    s.present = p.penalty_present;
+    s.pack = (uint32_t)n_eff | ((uint32_t)k_eff << 16) | (greedy ? (1u << 24) : 0u);
 }
 
 }  // namespace
@@ -163,47 +245,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
     // Check every row before enqueuing anything.
-    for (int64_t r = 0; r < B; ++r) {
-        const rts_row_params &p = params[r];
-        const long long rr = (long long)r;
-        if (std::isnan(p.temperature) || std::isinf(p.temperature))
-            return fail(RTS_EINVAL, "row %lld: temperature is not finite", rr);
-        const bool greedy = !(p.temperature > 0.0f);
-        if (!greedy && (p.top_k < 1 || p.top_k > RTS_MAX_TOP_K))
-            return fail(RTS_EINVAL, "row %lld: top_k = %d outside 1..64 on a sampled row", rr, p.top_k);
-        if (!(p.top_p > 0.0f && p.top_p <= 1.0f))
-            return fail(RTS_EINVAL, "row %lld: top_p = %g outside (0, 1]", rr, (double)p.top_p);
-        if (!(p.min_p >= 0.0f && p.min_p <= 1.0f))
-            return fail(RTS_EINVAL, "row %lld: min_p = %g outside [0, 1]", rr, (double)p.min_p);
-        if (!(p.penalty_repeat > 0.0f) || std::isinf(p.penalty_repeat))
-            return fail(RTS_EINVAL, "row %lld: penalty_repeat = %g must be finite > 0", rr,
-                        (double)p.penalty_repeat);
-        if (!std::isfinite(p.penalty_freq) || !std::isfinite(p.penalty_present))
-            return fail(RTS_EINVAL, "row %lld: penalty_freq / penalty_present not finite", rr);
-        if (p.penalty_last_n < -1)
-            return fail(RTS_EINVAL, "row %lld: penalty_last_n = %d < -1", rr, p.penalty_last_n);
-        if (p.history_row < -1)
-            return fail(RTS_EINVAL, "row %lld: history_row = %d < -1", rr, p.history_row);
-        if (p.reserved != 0) return fail(RTS_EINVAL, "row %lld: reserved field is not 0", rr);
-        if (p.history_row >= 0) {
-            if (history == nullptr || history_len == nullptr)
-                return fail(RTS_EINVAL, "row %lld: history_row set without history", rr);
-            if (p.history_row >= H)
-                return fail(RTS_EINVAL, "row %lld: history_row = %d >= H = %lld", rr,
-                            p.history_row, (long long)H);
-            const int32_t hl = history_len[p.history_row];
-            if (hl < 0 || hl > ldh)
-                return fail(RTS_EINVAL, "history row %d: length %d outside [0, ldh = %lld]",
-                            p.history_row, hl, (long long)ldh);
-            if ((int64_t)p.history_row * ldh + hl > 0x7FFFFFFFLL)
-                return fail(RTS_EINVAL, "row %lld: history offset of 2^31 ids or more", rr);
-            const int64_t n_eff = p.penalty_last_n < 0 ? hl
-                                  : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
-            if (n_eff > RTS_MAX_WINDOW)
-                return fail(RTS_EINVAL, "row %lld: penalty window of %lld ids > %d", rr,
-                            (long long)n_eff, RTS_MAX_WINDOW);
-        }
-    }
+    if (const int e = check_rows(B, params, history, H, ldh, history_len)) return e;
 
     char *ws = static_cast<char *>(workspace);
     const rts::WsLayout L = rts::ws_layout(B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch, V);
@@ -250,32 +292,10 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             a.lp_ids = lp->top_n > 0 ? lp->top_ids + r0 * lp->top_n : nullptr;
             a.lp_top = lp->top_n > 0 ? lp->top_lp + r0 * lp->top_n : nullptr;
         }
-        for (int i = 0; i < rows; ++i) {
-            const rts_row_params &p = params[r0 + i];
-            rts::SampleRow &s = a.row[i];
-            const bool greedy = !(p.temperature > 0.0f);
-            const int64_t k_eff = greedy ? 1 : (p.top_k < V ? p.top_k : V);
-            int64_t n_eff = 0, hist_off = 0;
-            const bool neutral = p.penalty_repeat == 1.0f && p.penalty_freq == 0.0f &&
-                                 p.penalty_present == 0.0f;
-            if (p.history_row >= 0 && !neutral) {
-                const int32_t hl = history_len[p.history_row];
-                n_eff = p.penalty_last_n < 0 ? hl : (p.penalty_last_n < hl ? p.penalty_last_n : hl);
-                hist_off = (int64_t)p.history_row * ldh + (hl - n_eff);
-            }
-            s.seed = p.seed;
-            s.counter = p.counter;
-            s.hist_off = (int32_t)hist_off;
-            s.allowed_off = allowed ? (int32_t)allowed_off[r0 + i] : 0;
-            s.allowed_cnt = allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0;
-            s.lnp = logf(p.min_p);
-            s.top_p = p.top_p;
-            s.temperature = p.temperature;
-            s.rep = p.penalty_repeat;
-            s.freq = p.penalty_freq;
-            s.present = p.penalty_present;
-            s.pack = (uint32_t)n_eff | ((uint32_t)k_eff << 16) | (greedy ? (1u << 24) : 0u);
-        }
+        for (int i = 0; i < rows; ++i)
+            pack_row(a.row[i], params[r0 + i], V, history_len, ldh,
+                     allowed ? (int32_t)allowed_off[r0 + i] : 0,
+                     allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0);
         const int e = rts::launch_sample(a, ept, is_vec_ok(a.logits, ld), stream);
         if (e != 0)
             return fail(RTS_EDEVICE, "sample launch (rows %lld..%lld): %s", (long long)r0,
@@ -390,6 +410,58 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
         }
         const int e = flush();
         if (e != 0) return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    return RTS_OK;
+}
+
+int rts_sample_tokens_prior(int design, const float *logits, int64_t B, int64_t V, int64_t ld,
+                            const rts_row_params *params,
+                            const int32_t *history, int64_t H, int64_t ldh,
+                            const int32_t *history_len,
+                            int32_t *token, int32_t *counts, int32_t *kept_ids,
+                            float *kept_logits, uint32_t *philox_x0,
+                            void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (design < RTS_PRIOR_THREAD || design > RTS_PRIOR_RECOUNT)
+        return fail(RTS_EINVAL, "design = %d outside 1..3", design);
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (B == 0) return RTS_OK;
+    if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
+    if (V <= 0 || V > (1 << 20)) return fail(RTS_EINVAL, "V = %lld out of (0, 2^20]", (long long)V);
+    if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
+    if (logits == nullptr || params == nullptr || token == nullptr || workspace == nullptr)
+        return fail(RTS_EINVAL, "logits, params, token and workspace must not be NULL");
+    if (H < 0 || ldh < 0) return fail(RTS_EINVAL, "H = %lld, ldh = %lld", (long long)H, (long long)ldh);
+    size_t need = 0;
+    rts_workspace_bytes(B, V, &need);
+    if (ws_bytes < need)
+        return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+    if (const int e = check_rows(B, params, history, H, ldh, history_len)) return e;
+    // the row's penalty bitmap lives in LDS beside the selection's own
+    const size_t lds = design == RTS_PRIOR_RECOUNT ? 0 : (size_t)((V + 31) / 32) * 4u;
+    if (lds + rts::kAllowedStaticLds > max_lds_per_block())
+        return fail(RTS_EINVAL, "V = %lld: the penalty bitmap does not fit in LDS", (long long)V);
+
+    char *ws = static_cast<char *>(workspace);
+    for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
+        const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
+        rts::SampleArgs a;
+        std::memset(&a, 0, sizeof a);
+        a.logits = logits + r0 * ld;
+        a.ld = ld;
+        a.history = history;
+        a.tickets = reinterpret_cast<uint32_t *>(ws);
+        a.token = token + r0;
+        a.counts = counts ? counts + 3 * r0 : nullptr;
+        a.kept_ids = kept_ids ? kept_ids + rts::kMaxK * r0 : nullptr;
+        a.kept_logits = kept_logits ? kept_logits + rts::kMaxK * r0 : nullptr;
+        a.philox_x0 = philox_x0 ? philox_x0 + r0 : nullptr;
+        a.V = (int32_t)V;
+        a.rows = rows;
+        for (int i = 0; i < rows; ++i) pack_row(a.row[i], params[r0 + i], V, history_len, ldh, 0, 0);
+        const int e = rts::launch_prior(a, design, lds, stream);
+        if (e != 0) return fail(RTS_EDEVICE, "prior-design launch: %s", hipGetErrorString((hipError_t)e));
     }
     return RTS_OK;
 }

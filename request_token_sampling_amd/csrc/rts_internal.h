@@ -155,6 +155,14 @@ int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s);
 int launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
+
+// The pages' earlier designs (rts_sample_tokens_prior): one thread per row,
+// one workgroup per row with k argmax rounds, and the latter with the
+// per-candidate penalty recount instead of the bitmap.
+constexpr int PRIOR_THREAD = 1;
+constexpr int PRIOR_BLOCK = 2;
+constexpr int PRIOR_RECOUNT = 3;
+int launch_prior(const SampleArgs &a, int design, size_t lds_bytes, hipStream_t s);
 int launch_read_rows(const float *x, int rows, int V, int64_t ld, int nchunks, int out_stride,
                      float *out, int ept, bool vec, bool early, hipStream_t s);
 

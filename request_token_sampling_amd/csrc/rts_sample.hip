@@ -16,7 +16,7 @@
 // counter may live in device memory, where the call advances it, so a
 // captured graph replaying the call keeps drawing fresh numbers ("Problem":
 // a captured sampler would otherwise repeat its draws).
-#include "rts_select.h"
+#include "rts_epilogue.h"
 
 namespace rts {
 
@@ -28,20 +28,6 @@ struct SampleSmem {
     uint64_t raw_keys[LP ? 4 * kRegion : 1];  // candidates of the raw top-K
     uint32_t raw_cnt[4];
 };
-
-// llama.cpp-style penalty of an id seen c > 0 times in the window: the repeat
-// penalty divides a positive logit and multiplies a non-positive one, the
-// frequency term scales with the count and the presence term is charged once.
-// Every operation is rounded to fp32 (the build disables contraction).
-__device__ __forceinline__ float penalize(float v, uint32_t c, float rep, float freq,
-                                          float present)
-{
-    v = (v <= 0.0f) ? v * rep : v / rep;
-    float t = (float)c * freq;
-    t = t + present;
-    v = v - t;
-    return sanitize(v);
-}
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,104 +52,6 @@ __device__ __forceinline__ void load_chunk(const float *x, int base, int V, floa
                 v[4 * q + s] = (i0 + s < V) ? x[i0 + s] : __builtin_nanf("");
         }
     }
-}
-
-// Verify windows (page "#19 ...", "What changed": the emitted tokens are the
-// target's own samples; page "#559 ...", "Not done (yet)": a sampled row is
-// accepted when its pick equals the draft).  Run by wave 0 of a row's merging
-// workgroup once the row's token is published: the window's last row to get
-// here counts the leading rows whose token equals their draft and writes the
-// number of tokens the window emits.
-__device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32_t tok)
-{
-    const int lane = lane_id();
-    const int w = slot / a.window;
-    uint32_t last = 0u;
-    if (lane == 0) {
-        wait_stores_complete();
-        const uint32_t old = __hip_atomic_fetch_add(&a.wtickets[w * kTicketStride], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = (old == (uint32_t)a.window - 1u) ? 1u : 0u;
-    }
-    if (lane_u32(last, 0) == 0u) return;
-    const int r0 = w * a.window;
-    bool miss = false;
-    if (lane < a.window - 1) {
-        const int32_t t = (r0 + lane == slot) ? tok : read_published_i32(&a.token[r0 + lane]);
-        miss = t != a.draft[r0 + lane];
-    }
-    const uint64_t b = __ballot(miss);
-    if (lane == 0) {
-        a.accepted[w] = b ? __ffsll((unsigned long long)b) : a.window;
-        a.wtickets[w * kTicketStride] = 0u;
-    }
-}
-
-// The cuts and the draw, run by wave 0 of the row's last workgroup on the
-// merged kept sequence sm.sel[0..k).  Leaves the sampled token in sm.flag.
-__device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
-                                         int slot, int k, bool greedy, uint64_t ctr, uint32_t x0)
-{
-    const int lane = lane_id();
-    const uint64_t key = (lane < k) ? sm.sel[lane] : 0ull;
-    const bool valid = key != 0ull;
-    const int32_t id = valid ? (int32_t)key_index(key) : -1;
-    const float y = valid ? key_logit(key) : -INFINITY;
-    if (a.kept_ids) a.kept_ids[(int64_t)slot * kMaxK + lane] = id;
-    if (a.kept_logits) a.kept_logits[(int64_t)slot * kMaxK + lane] = y;
-    // The kept sequence holds k keys, or fewer when a row's allowed ids are
-    // fewer than k (zero keys sort last); an empty one samples nothing.
-    k = __popcll(__ballot(valid));
-
-    const float y0 = lane_f32(y, 0);
-    int m = k > 0 ? 1 : 0, n = m, pick = 0;
-    if (!greedy && k > 0) {
-        // Everything that does not depend on the cuts first: top_p weights
-        // exp(y - y0) and tempered weights exp((y - y0) / T).
-        const double dy = (double)y - (double)y0;
-        const bool head_masked = (y0 == -INFINITY);
-        const double d = (lane < k && !head_masked) ? exp(dy) : 0.0;
-        const double w = (lane < k && !head_masked) ? exp(dy / (double)R.temperature) : 0.0;
-        // min_p: keep the prefix with logit >= head + logf(min_p), in fp32.
-        const float thr = y0 + R.lnp;
-        m = __popcll(__ballot(lane < k && y >= thr));
-        m = m < 1 ? 1 : m;
-        // top_p: shortest prefix of the min_p survivors whose fp64 softmax
-        // mass reaches top_p; a masked head (-inf) keeps one candidate.
-        n = m;
-        if (head_masked) {
-            n = 1;
-        } else if (!(R.top_p >= 1.0f)) {
-            const double S = wave_scan_f64(lane < m ? d : 0.0);
-            const double Z = lane_f64(S, m - 1);
-            const uint64_t b = __ballot(lane < m && S / Z >= (double)R.top_p);
-            n = b ? __ffsll((unsigned long long)b) : m;
-        }
-        // temperature, then the draw: u = x0 / 2^32 against the tempered CDF.
-        const double u = (double)x0 * (1.0 / 4294967296.0);
-        pick = n - 1;
-        if (n > 1) {
-            const double S = wave_scan_f64(lane < n ? w : 0.0);
-            const double Z = lane_f64(S, n - 1);
-            const uint64_t b = __ballot(lane < n - 1 && S / Z > u);
-            if (b) pick = __ffsll((unsigned long long)b) - 1;
-        }
-    }
-    const int32_t tok = lane_i32(id, pick);
-    if (lane == 0) {
-        sm.flag = (uint32_t)tok;
-        if (a.window > 0) publish_i32(&a.token[slot], tok);  // read by the window's last row
-        else a.token[slot] = tok;
-        if (a.counts) {
-            a.counts[3 * (int64_t)slot + 0] = k;
-            a.counts[3 * (int64_t)slot + 1] = m;
-            a.counts[3 * (int64_t)slot + 2] = n;
-        }
-        if (a.philox_x0) a.philox_x0[slot] = x0;
-        if (a.counters) a.counters[slot] = ctr + (uint64_t)a.counter_stride;
-        a.tickets[slot * kTicketStride] = 0u;  // ready for the next launch on this workspace
-    }
-    if (a.window > 0) window_step(a, slot, tok);
 }
 
 template <int EPT, bool VEC, bool LP>

@@ -253,3 +253,19 @@ def test_read_rows_refusals():
     assert L.rts_read_rows(FAKE, 1, 100, 99, FAKE, None) == R.RTS_EINVAL and "ld" in last_error()
     assert L.rts_read_rows(None, 1, 100, 100, FAKE, None) == R.RTS_EINVAL
     assert L.rts_read_rows(FAKE, 1, 100, 100, None, None) == R.RTS_EINVAL
+
+
+def test_prior_designs_refusals():
+    L = R.lib()
+    arr = R.row_params([dict(SAMPLED)])
+
+    def call(design=2, B=1, V=1000, ld=1000, rows=arr):
+        return L.rts_sample_tokens_prior(design, FAKE, B, V, ld, rows, None, 0, 0, None, FAKE,
+                                         None, None, None, None, FAKE, BIG_WS, None)
+    assert call(design=0) == R.RTS_EINVAL and "design" in last_error()
+    assert call(design=4) == R.RTS_EINVAL
+    assert call(V=(1 << 20) + 1, ld=(1 << 20) + 1) == R.RTS_EINVAL
+    assert call(ld=10) == R.RTS_EINVAL
+    assert call(B=0) == R.RTS_OK
+    assert call(rows=R.row_params([dict(SAMPLED, top_k=65)])) == R.RTS_EINVAL
+    assert "top_k" in last_error()
