@@ -254,7 +254,11 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                                           : rts::kRowsPerLaunch;
     for (int64_t r0 = 0; r0 < B; r0 += per_launch) {
         const int rows = (int)((B - r0) < per_launch ? (B - r0) : per_launch);
-        const int ept = choose_ept(rows, V);
+        const bool vec = is_vec_ok(logits + r0 * ld, ld);
+        int ept = choose_ept(rows, V);
+        // rows read element by element keep 4,096-element chunks: at 8,192 the
+        // scalar-load variant spills registers
+        if (!vec && ept > 16) ept = 16;
         rts::SampleArgs a;
         std::memset(&a, 0, sizeof a);
         a.logits = logits + r0 * ld;
@@ -296,7 +300,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             pack_row(a.row[i], params[r0 + i], V, history_len, ldh,
                      allowed ? (int32_t)allowed_off[r0 + i] : 0,
                      allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0);
-        const int e = rts::launch_sample(a, ept, is_vec_ok(a.logits, ld), stream);
+        const int e = rts::launch_sample(a, ept, vec, stream);
         if (e != 0)
             return fail(RTS_EDEVICE, "sample launch (rows %lld..%lld): %s", (long long)r0,
                         (long long)(r0 + rows - 1), hipGetErrorString((hipError_t)e));
@@ -331,10 +335,10 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
     // Restricted rows take the gather-once kernel when their list is short
-    // enough and its LDS (bitmap + member list) fits, else the bitmap-walking
-    // kernel (bitmap only).
+    // enough, else the bitmap-walking kernel; both keep a vocabulary bitmap
+    // in LDS.
     const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
-    const size_t fast_lds = bitmap_bytes + (size_t)rts::kAllowedFast * 4u;
+    const size_t fast_lds = bitmap_bytes;
     bool any_restricted = false, fast_fits = false;
     if (allowed != nullptr) {
         if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");

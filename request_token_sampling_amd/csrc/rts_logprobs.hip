@@ -255,34 +255,14 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_wide_kernel(const Logp
     }
 }
 
-
-// Block-wide exclusive prefix of one count per thread (wave DPP scan, then the
-// wave totals through LDS); returns the thread's offset and the block total.
-__device__ __forceinline__ uint32_t block_excl_scan(SelectSmem &sm, uint32_t c, uint32_t *total)
-{
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const double incl = wave_scan_f64((double)c);   // exact for counts < 2^53
-    const uint32_t wincl = (uint32_t)incl;
-    if (lane == 63) sm.wave_cnt[wave] = wincl;
-    __syncthreads();
-    uint32_t base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t t = sm.wave_cnt[w];
-        base += (w < wave) ? t : 0u;
-        tot += t;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + wincl - c;
-}
-
-// One workgroup per restricted row with at most kAllowedFast listed ids.  The
-// named ids are marked in an LDS bitmap of the vocabulary (duplicates collapse,
-// foreign ids are ignored), the members are compacted in id-word order into an
-// LDS list, and their logits are gathered once, in one batch, into registers;
-// the max, the fp64 sum of exponentials and the top-K all run from there.
-// Dynamic LDS: the bitmap, then the member list.
+// One workgroup per restricted row with at most kAllowedFast listed ids.
+// Thread t reads listed ids t, t + 256, ... and gathers their logits at
+// once; marking each id in an LDS bitmap of the vocabulary makes the thread
+// that set its bit the id's owner, so duplicates count once and foreign ids
+// are ignored.  Which thread owns a duplicate depends on timing, so the sum
+// of exponentials is made order-free: each term is rounded to a multiple of
+// 2^-40 and the multiples, below 2^53 in total, add exactly in fp64.  The
+// max, the sum and the top-K all run from registers.  Dynamic LDS: the bitmap.
 __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobArgs a)
 {
     extern __shared__ uint32_t bm[];
@@ -294,58 +274,64 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
     const int V = a.V;
     const int K = a.top_n;
     const int nw = (V + 31) >> 5;
-    int32_t *list = reinterpret_cast<int32_t *>(bm + nw);
     const float *x = a.logits + (int64_t)row * a.ld;
+    // the token's logit, loaded now so its latency hides behind the rest
+    const int32_t t = a.tokens[row];
+    const float xt = (tid == 0 && t >= 0 && t < V) ? x[t] : 0.0f;
 
-    for (int w = tid; w < nw; w += kBlock) bm[w] = 0u;
-    __syncthreads();
+    // listed ids and their logits, all loads in flight together
     const int32_t *ids = a.allowed + R.allowed_off;
-    for (int j = tid; j < (int)R.allowed_cnt; j += kBlock) {
-        const int32_t id = ids[j];
-        if (id >= 0 && id < V) atomicOr(&bm[id >> 5], 1u << (id & 31));
-    }
-    __syncthreads();
-
-    // members of the thread's words, compacted in a fixed order
-    uint32_t mine = 0;
-    for (int w = tid; w < nw; w += kBlock) mine += (uint32_t)__popc(bm[w]);
-    uint32_t members = 0;
-    uint32_t pos = block_excl_scan(sm, mine, &members);
-    for (int w = tid; w < nw; w += kBlock) {
-        uint32_t bits = bm[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1u;
-            list[pos++] = (w << 5) + b;
-        }
-    }
-    __syncthreads();
-
-    // one batch of gathers: member f = tid + 256 * j
+    const int cnt = (int)R.allowed_cnt;
+    int32_t id[kAllowedPerThread];
     float v[kAllowedPerThread];
 #pragma unroll
     for (int j = 0; j < kAllowedPerThread; ++j) {
-        const uint32_t f = (uint32_t)(tid + j * kBlock);
-        v[j] = (f < members) ? sanitize(x[list[f]]) : __builtin_nanf("");
+        const int f = tid + j * kBlock;
+        id[j] = (f < cnt) ? ids[f] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < kAllowedPerThread; ++j)
+        v[j] = (id[j] >= 0 && id[j] < V) ? x[id[j]] : __builtin_nanf("");
+
+    for (int w = tid; w < nw; w += kBlock) bm[w] = 0u;
+    __syncthreads();
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kAllowedPerThread; ++j) {
+        bool owner = false;
+        if (id[j] >= 0 && id[j] < V) {
+            const uint32_t bit = 1u << (id[j] & 31);
+            owner = (atomicOr(&bm[id[j] >> 5], bit) & bit) == 0u;
+        }
+        v[j] = owner ? sanitize(v[j]) : __builtin_nanf("");  // NaN: not this thread's member
+        mine += owner ? 1u : 0u;
+    }
+
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kAllowedPerThread; ++j) lmax = (v[j] == v[j]) ? fmaxf(lmax, v[j]) : lmax;
     float *red = reinterpret_cast<float *>(sm.red);
     const float wm = wave_max_f32(lmax);
-    if (lane == 0) red[wave] = wm;
+    const double wn = wave_sum_f64((double)mine);
+    if (lane == 0) {
+        red[wave] = wm;
+        sm.wave_cnt[wave] = (uint32_t)wn;
+    }
     __syncthreads();
     const float Mf = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const uint32_t members = sm.wave_cnt[0] + sm.wave_cnt[1] + sm.wave_cnt[2] + sm.wave_cnt[3];
     const double M = (double)Mf;
+    constexpr double kUnit = 1099511627776.0;  // 2^40
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < kAllowedPerThread; ++j)
-        if (v[j] == v[j]) s += (Mf == -INFINITY) ? 1.0 : exp((double)v[j] - M);
+        if (v[j] == v[j]) s += (Mf == -INFINITY) ? 1.0 : rint((double)__expf(v[j] - Mf) * kUnit);
     s = wave_sum_f64(s);
     double *dred = reinterpret_cast<double *>(sm.cand);
     if (lane == 0) dred[wave] = s;
     __syncthreads();
-    const double S = (dred[0] + dred[1]) + (dred[2] + dred[3]);
+    double S = (dred[0] + dred[1]) + (dred[2] + dred[3]);
+    if (Mf != -INFINITY) S = S / kUnit;
     __syncthreads();
     const bool empty = members == 0u;
     const bool uniform = !empty && Mf == -INFINITY;
@@ -353,7 +339,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
 
     if (K > 0) {
         // top-K of the members: lane maxima -> threshold -> compaction -> rank
-        sm.lane_keys[tid] = ((uint32_t)tid < members) ? value_key(lmax) : 0u;
+        sm.lane_keys[tid] = (lmax == -INFINITY && mine == 0u) ? 0u : value_key(lmax);
         __syncthreads();
         const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
@@ -363,12 +349,11 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
         uint32_t wcnt = 0;
 #pragma unroll
         for (int j = 0; j < kAllowedPerThread; ++j) {
-            const uint32_t f = (uint32_t)(tid + j * kBlock);
             const bool c = v[j] >= tf;               // NaN (no member) never passes
             const uint64_t m = __ballot(c);
             if (m) {
                 const uint32_t p = wcnt + (uint32_t)__popcll(m & below);
-                if (c && p < (uint32_t)kCap) wc[p] = cand_key(v[j], (uint32_t)list[f]);
+                if (c && p < (uint32_t)kCap) wc[p] = cand_key(v[j], (uint32_t)id[j]);
                 wcnt += (uint32_t)__popcll(m);
             }
         }
@@ -384,9 +369,8 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
                 uint64_t best = 0;
 #pragma unroll
                 for (int j = 0; j < kAllowedPerThread; ++j) {
-                    const uint32_t f = (uint32_t)(tid + j * kBlock);
-                    if (f < members) {
-                        const uint64_t key = cand_key(v[j], (uint32_t)list[f]);
+                    if (v[j] == v[j]) {
+                        const uint64_t key = cand_key(v[j], (uint32_t)id[j]);
                         best = (key < prev && key > best) ? key : best;
                     }
                 }
@@ -399,10 +383,9 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
     }
 
     if (tid == 0) {
-        const int32_t t = a.tokens[row];
         float lp = -INFINITY;
         if (t >= 0 && t < V && ((bm[t >> 5] >> (t & 31)) & 1u))
-            lp = uniform ? (float)(-L) : (float)((double)sanitize(x[t]) - L);
+            lp = uniform ? (float)(-L) : (float)((double)sanitize(xt) - L);
         a.token_lp[row] = lp;
     }
     if (tid < K) {

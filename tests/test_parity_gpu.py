@@ -341,3 +341,21 @@ def test_read_rows_measuring_stick(B, Vx):
     nch = int(np.sum(~np.isnan(cm[0])))             # entries past the chunk count stay NaN
     assert nch >= 1
     assert np.array_equal(np.max(cm[:, :nch], axis=1), np.max(x, axis=1))
+
+
+def test_allowed_logprobs_are_deterministic_with_duplicates():
+    """Which thread owns a duplicated id depends on timing; the outputs must
+    not: repeated calls agree bit for bit and with the oracle."""
+    rng = np.random.default_rng(13)
+    Vx = 50000
+    x = rng.normal(0, 3, (8, Vx)).astype(np.float32)
+    base = [rng.choice(Vx, 300, replace=False).astype(np.int32) for _ in range(8)]
+    lists = [np.concatenate([b, b, b[:100], b[::-1]]) for b in base]      # 1,000 listed ids
+    tokens = np.array([int(b[0]) for b in base], np.int32)
+    say("case allowed determinism")
+    first = gpu_logprobs(x, tokens, 20, lists)
+    for _ in range(3):
+        again = gpu_logprobs(x, tokens, 20, lists)
+        for k in first:
+            assert first[k].tobytes() == again[k].tobytes(), k
+    compare_logprobs(first, O.token_logprobs(x, tokens, 20, lists), "allowed dup")
