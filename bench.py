@@ -73,13 +73,17 @@ class Workload:
         hist = hist_len = None
         lp = None
         spec = {}
+        self.alt_passes = []
         if name == "single_stream":
             w = W.single_stream()
             x = w["logits"]
-            passes = [("sampled", w["sampled"], 1, 1), ("greedy", w["greedy"], 0, 1)]
+            # the sampled and the greedy pass as two parameter rows of one launch
+            # over the one logits row (ld = 0); the two-launch form is timed beside
+            passes = [("sampled+greedy", w["sampled"] + w["greedy"], 1, 1)]
+            self.alt_passes = [("sampled", w["sampled"]), ("greedy", w["greedy"])]
             self.desc = ("single stream: 1 row, V=248,320 fp32 N(0,3) with 3 spiked heads; "
                          "top_k 20, top_p 0.8, min_p 0, temperature 0.7, no penalties; "
-                         "plus a greedy pass over the same row")
+                         "plus a greedy pass over the same row (both in one launch)")
         elif name == "window":
             vw = W.VerifyWindows()
             x = vw.next_logits()
@@ -115,19 +119,22 @@ class Workload:
         self.copies = base.unsqueeze(0).repeat(self.ncopies, 1, 1)
         self.hist = None if hist is None else torch.from_numpy(np.asarray(hist, np.int32)).to(dev)
         self.hist_len = hist_len
-        self.first_params = passes[0][1]
-        self.ws = R.make_workspace(self.B, self.V, dev)
+        self.first_params = self.alt_passes[0][1] if self.alt_passes else passes[0][1]
+        self.ws = R.make_workspace(max([self.B] + [len(p[1]) for p in passes]), self.V, dev)
         self.calls, self.labels = [], []
         self.sampled_rows = 0
         for label, params, counted, stride in passes:
             ctr = torch.tensor([p.get("counter", 0) for p in params], dtype=torch.int64,
                                device=dev)
-            self.calls.append(R.SampleCall(self.copies[0], params, self.hist, hist_len,
-                                           workspace=self.ws, counters=ctr,
+            self.calls.append(R.SampleCall(self.view(self.copies[0], len(params)), params,
+                                           self.hist, hist_len, workspace=self.ws, counters=ctr,
                                            counter_stride=stride,
                                            logprobs=None if lp is None else lp[0], **spec))
             self.labels.append(label)
             self.sampled_rows += counted
+        self.param_rows = sum(c.B for c in self.calls)
+        self.alt_calls = [R.SampleCall(self.copies[0], params, self.hist, hist_len,
+                                       workspace=self.ws) for _, params in self.alt_passes]
         self.lp_calls = []
         if lp is not None:
             top_n, ids, off = lp
@@ -138,10 +145,16 @@ class Workload:
         self.passes = [l for l in self.labels] + (["logprobs_allowed"] if self.lp_calls else [])
         self.torch = torch
 
+    @staticmethod
+    def view(x, rows):
+        """The logits as `rows` parameter rows: the batch itself, or its one
+        row broadcast (ld = 0) when several parameter rows share it."""
+        return x if rows == x.shape[0] else x.expand(rows, -1)
+
     def step(self, i):
         x = self.copies[i % self.ncopies]
         for c in self.calls:
-            c.logits = x
+            c.logits = self.view(x, c.B)
             c()
         for c in self.lp_calls:
             c.logits = x
@@ -196,7 +209,7 @@ def kernel_durations(wl, steps):
             torch.cuda._sleep(int(steps * 0.05e-3 * 2.0e9))
         e0.record()
         for i in range(steps):
-            c.logits = wl.copies[i % wl.ncopies]
+            c.logits = wl.view(wl.copies[i % wl.ncopies], c.B)
             c()
         e1.record()
         torch.cuda.synchronize()
@@ -208,7 +221,7 @@ def roofline(wl, kern_ms):
     """HBM roofline of the sampler kernel: algorithmic bytes per launch (one
     read of every logit row, plus outputs) over its average launch duration
     (all sampler launches of a step: they are one kernel)."""
-    out_bytes = wl.B * (4 + 12 + 256 + 256 + 4 + 8)
+    out_bytes = wl.param_rows * (4 + 12 + 256 + 256 + 4 + 8)
     alg = wl.B * wl.row_bytes + out_bytes
     avg_ms = sum(kern_ms) / len(kern_ms)
     achieved = alg / (avg_ms * 1e-3) / 1e9
@@ -253,7 +266,7 @@ def per_launch_us(wl, call, launches):
     """Average time of `launches` back-to-back launches of one prepared call
     over rotating copies, between two events with the host enqueued ahead."""
     torch = wl.torch
-    call.logits = wl.copies[0]
+    call.logits = wl.view(wl.copies[0], call.B)
     call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,7 +274,7 @@ def per_launch_us(wl, call, launches):
         torch.cuda._sleep(int(launches * 0.05e-3 * 2.0e9))
     e0.record()
     for i in range(launches):
-        call.logits = wl.copies[i % wl.ncopies]
+        call.logits = wl.view(wl.copies[i % wl.ncopies], call.B)
         call()
     e1.record()
     torch.cuda.synchronize()
@@ -296,11 +309,35 @@ def ablations(dev):
     return out
 
 
+def time_alt_graph(wl, steps):
+    """Per-step wall time with the passes of a step as separate launches
+    (single stream: the sampled pass, then the greedy pass), graph-replayed."""
+    torch = wl.torch
+    for c in wl.alt_calls:
+        c()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            for c in wl.alt_calls:
+                c.logits = wl.copies[i % wl.ncopies]
+                c()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    return wall / steps
+
+
 def measure(wl, steps, warmup):
     eager = time_eager(wl, steps, warmup)
     graph = time_graph(wl, steps)
     kern = kernel_durations(wl, min(steps, 500))
-    return dict(graph_wall=graph, eager_wall=eager, kern_ms=kern, floor=read_floor(wl))
+    alt = time_alt_graph(wl, steps) if wl.alt_calls else None
+    return dict(graph_wall=graph, eager_wall=eager, kern_ms=kern, floor=read_floor(wl), alt=alt)
 
 
 def read_traffic(workload):
@@ -496,6 +533,10 @@ def main():
         "eager": {"value": round(wl.sampled_rows * args.steps / m["eager_wall"], 1),
                   "ms_per_step": round(m["eager_wall"] / args.steps * 1e3, 5)},
     }
+    if m["alt"] is not None:
+        line["separate_launches"] = {"value": round(wl.sampled_rows / m["alt"], 1),
+                                     "ms_per_step": round(m["alt"] * 1e3, 5),
+                                     "passes": [l for l, _ in wl.alt_passes]}
     if not args.no_extra:
         extra = {}
         for name in ("batch", "stress", "window"):

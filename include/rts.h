@@ -133,7 +133,9 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * The sampling chain over B rows.
- *   logits      device fp32 [B][ld], row-major, ld >= V; 0 < V < 2^31.
+ *   logits      device fp32 [B][ld], row-major, ld >= V; 0 < V < 2^31.  ld = 0
+ *               makes every row read row 0: several parameter sets (several
+ *               samples, a sampled and a greedy pass) over one distribution.
  *   params      host [B].
  *   history     device int32 [H][ldh] or NULL when no row names one; row h
  *               holds history_len[h] ids, oldest first.  The window of a row
@@ -159,7 +161,7 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
  *   lp          host, or NULL for no logprobs: see rts_logprob_request.
  *   ex          host, or NULL: verify windows and allowed-id masks, see
  *               rts_sample_extras.
- * Errors: RTS_EINVAL for B < 0, V out of range, ld < V, NULL logits/token,
+ * Errors: RTS_EINVAL for B < 0, V out of range, 0 < ld < V, NULL logits/token,
  * a row with NaN or infinite temperature, top_k outside 1..64 on a sampled
  * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
  * non-finite penalties, history_row >= H or set without history, a window

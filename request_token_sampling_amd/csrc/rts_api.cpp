@@ -203,7 +203,10 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (B == 0) return RTS_OK;
     if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
     if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
-    if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
+    // ld = 0: every row reads logits row 0 (several parameter sets over one
+    // distribution, e.g. several samples of one request)
+    if (ld != 0 && ld < V)
+        return fail(RTS_EINVAL, "ld = %lld is neither 0 nor >= V = %lld", (long long)ld, (long long)V);
     if (logits == nullptr) return fail(RTS_EINVAL, "logits is NULL");
     if (params == nullptr) return fail(RTS_EINVAL, "params is NULL");
     if (token == nullptr) return fail(RTS_EINVAL, "token is NULL");

@@ -113,6 +113,7 @@ def test_bad_shapes_and_pointers():
     assert sample(rows, V=0) == R.RTS_EINVAL
     assert sample(rows, V=2**31) == R.RTS_EINVAL
     assert sample(rows, ld=999) == R.RTS_EINVAL and "ld" in last_error()
+    assert sample(rows, ld=1) == R.RTS_EINVAL and "ld" in last_error()
     assert sample(rows, logits=None) == R.RTS_EINVAL and "logits" in last_error()
     assert sample(rows, token=None) == R.RTS_EINVAL and "token" in last_error()
     assert sample(rows, ws=None) == R.RTS_EINVAL

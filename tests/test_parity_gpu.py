@@ -359,3 +359,17 @@ def test_allowed_logprobs_are_deterministic_with_duplicates():
         for k in first:
             assert first[k].tobytes() == again[k].tobytes(), k
     compare_logprobs(first, O.token_logprobs(x, tokens, 20, lists), "allowed dup")
+
+
+def test_broadcast_rows_share_one_logits_row():
+    """ld = 0: several parameter rows (a sampled and a greedy pass, several
+    samples) over one logits row equal the same rows over copies of it."""
+    w = W.single_stream()
+    x1 = w["logits"]
+    params = w["sampled"] + w["greedy"] + [sampled(top_k=5, counter=c, seed=3) for c in range(3)]
+    B = len(params)
+    say("case broadcast rows", B)
+    out = R.sample_tokens(to_dev(x1).expand(B, -1), params)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    compare_sample(g, oracle_sample(np.repeat(x1, B, axis=0), params), "broadcast")
