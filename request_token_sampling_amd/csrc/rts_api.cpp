@@ -280,7 +280,8 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.nchunks = (int32_t)chunks_for(V, ept);
         a.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
         a.rows = rows;
-        a.early_xcds = rows * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
+        a.chunk_major = (ld == 0 && rows > 1) ? 1 : 0;
+        a.early_xcds = rts::sample_work(rows, a.nchunks, 1, a.chunk_major) <= rts::kEarlyXcdWork ? 1 : 0;
         a.allowed = allowed;
         if (window > 0) {
             a.window = window;

@@ -108,7 +108,7 @@ struct SampleArgs {
     int32_t *accepted;       // tokens emitted per window, window 0 of this launch
     uint32_t *wtickets;      // workspace: one ticket per window slot
     int32_t window;          // rows per verify window; 0: none
-    int32_t pad3_;
+    int32_t chunk_major;     // 1: rows share one logits row; a chunk's rows share an XCD
     SampleRow row[kRowsPerLaunch];
 };
 // HIP passes at most 4 KiB of kernel arguments.
@@ -149,6 +149,18 @@ constexpr int kEarlyXcdWork = 64;
 
 // Grid for `work` workgroups, padded for early-XCD placement when it applies.
 inline unsigned grid_for(int work, int early) { return early ? (unsigned)(((work + 1) / 2) * 8) : (unsigned)work; }
+
+// XCDs a launch's work is spread over (logical_block): 2 for early-XCD launches.
+__host__ __device__ inline int xcds_used(int early) { return early ? 2 : 8; }
+
+// Logical workgroups of a sampling launch.  Chunk-major launches (rows that
+// share one logits row) pad the chunk count to a multiple of the XCDs used.
+__host__ __device__ inline int sample_work(int rows, int nchunks, int early, int chunk_major)
+{
+    if (!chunk_major) return rows * nchunks;
+    const int P = xcds_used(early);
+    return rows * ((nchunks + P - 1) / P) * P;
+}
 
 // Launchers (return a hipError_t as int).
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);

@@ -63,9 +63,20 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
 
     const int tid = threadIdx.x;
     const int lb = logical_block(a.early_xcds);
-    if (lb < 0 || lb >= a.rows * a.nchunks) return;  // padding workgroup
-    const int slot = lb / a.nchunks;
-    const int chunk = lb - slot * a.nchunks;
+    if (lb < 0 || lb >= sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major)) return;
+    int slot, chunk;
+    if (a.chunk_major) {
+        // Rows that share one logits row: the workgroups of one chunk for all
+        // rows land on one XCD, so the chunk is fetched from HBM once and the
+        // other rows read it from that XCD's L2.
+        const int P = xcds_used(a.early_xcds), x = lb % P, q = lb / P;
+        slot = q % a.rows;
+        chunk = (q / a.rows) * P + x;
+        if (chunk >= a.nchunks) return;  // padding workgroup
+    } else {
+        slot = lb / a.nchunks;
+        chunk = lb - slot * a.nchunks;
+    }
     const SampleRow R = a.row[slot];
     const int V = a.V;
     const int n_eff = (int)(R.pack & 0xFFFFu);
@@ -223,7 +234,9 @@ template <int EPT, bool VEC, bool LP>
 static int launch_t(const SampleArgs &a, hipStream_t s)
 {
     hipLaunchKernelGGL((sample_kernel<EPT, VEC, LP>),
-                       dim3(grid_for(a.rows * a.nchunks, a.early_xcds)), dim3(kBlock), 0, s, a);
+                       dim3(grid_for(sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major),
+                                     a.early_xcds)),
+                       dim3(kBlock), 0, s, a);
     return (int)hipGetLastError();
 }
 
