@@ -361,15 +361,44 @@ def test_allowed_logprobs_are_deterministic_with_duplicates():
     compare_logprobs(first, O.token_logprobs(x, tokens, 20, lists), "allowed dup")
 
 
-def test_broadcast_rows_share_one_logits_row():
+def _mixed_params(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for r in range(n):
+        if r % 7 == 3:
+            out.append(W.row_params())  # greedy
+        else:
+            out.append(sampled(temperature=float(rng.uniform(0.2, 1.5)),
+                               top_k=int(rng.integers(1, 65)), top_p=float(rng.uniform(0.5, 1.0)),
+                               min_p=float(rng.uniform(0.0, 0.2)), seed=int(rng.integers(1, 1 << 40)),
+                               counter=r))
+    return out
+
+
+@pytest.mark.parametrize("case", ["pair", "five", "max_rows", "two_launches", "ragged_10007",
+                                  "ragged_70001"])
+def test_broadcast_rows_share_one_logits_row(case):
     """ld = 0: several parameter rows (a sampled and a greedy pass, several
-    samples) over one logits row equal the same rows over copies of it."""
+    samples) over one logits row equal the same rows over copies of it.
+    Covers the chunk-major placement on two XCDs (two rows) and on eight,
+    chunk counts that do not divide evenly, and more rows than one launch."""
     w = W.single_stream()
     x1 = w["logits"]
-    params = w["sampled"] + w["greedy"] + [sampled(top_k=5, counter=c, seed=3) for c in range(3)]
+    if case == "pair":
+        params = w["sampled"] + w["greedy"]
+    elif case == "five":
+        params = w["sampled"] + w["greedy"] + [sampled(top_k=5, counter=c, seed=3) for c in range(3)]
+    elif case == "max_rows":
+        params = _mixed_params(64, 5)
+    elif case == "two_launches":
+        params = _mixed_params(70, 6)
+    else:
+        Vx = int(case.split("_")[1])
+        x1 = np.random.default_rng(Vx).normal(0.0, 3.0, (1, Vx)).astype(np.float32)
+        params = _mixed_params(3 if Vx < 20000 else 2, Vx)
     B = len(params)
-    say("case broadcast rows", B)
+    say("case broadcast rows", case, B, x1.shape[1])
     out = R.sample_tokens(to_dev(x1).expand(B, -1), params)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in out.items()}
-    compare_sample(g, oracle_sample(np.repeat(x1, B, axis=0), params), "broadcast")
+    compare_sample(g, oracle_sample(np.repeat(x1, B, axis=0), params), "broadcast " + case)
