@@ -183,8 +183,10 @@ __device__ __forceinline__ float wave_sum_f32(float x)
 }
 
 // The value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}: DPP quad
-// permutes for 1 and 2, row shifts for 4, a row rotation for 8, an LDS-free
-// swizzle within 32 lanes for 16 and a lane permute for 32.
+// permutes for 1 and 2, row shifts for 4, a row rotation for 8, and for 16
+// and 32 gfx950's row-swap permutes (v_permlane16_swap / v_permlane32_swap
+// of a register with itself leave the even and the odd 16-lane rows, or the
+// two 32-lane halves, in every lane), all in the VALU.
 template <int J>
 __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x)
 {
@@ -198,14 +200,18 @@ __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t x)
     } else if constexpr (J == 8) {
         return dpp_u64<0x128>(x);  // row_ror:8
     } else if constexpr (J == 16) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)x, 0x401F);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(x >> 32), 0x401F);
-        return ((uint64_t)hi << 32) | lo;
+        // r[0]: rows 0, 0, 2, 2 of x; r[1]: rows 1, 1, 3, 3
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+        const bool odd = (lane_id() & 16) != 0;
+        return ((uint64_t)(odd ? hi[0] : hi[1]) << 32) | (odd ? lo[0] : lo[1]);
     } else {
         static_assert(J == 32, "lane distance");
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, 32);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), 32);
-        return ((uint64_t)hi << 32) | lo;
+        // r[0]: lanes 0-31 of x in both halves; r[1]: lanes 32-63
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+        const bool upper = (lane_id() & 32) != 0;
+        return ((uint64_t)(upper ? hi[0] : hi[1]) << 32) | (upper ? lo[0] : lo[1]);
     }
 }
 

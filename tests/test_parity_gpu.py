@@ -164,6 +164,19 @@ def test_all_equal_rows_force_fallbacks():
     assert list(g["kept_ids"][0][:64]) == list(range(64))
 
 
+@pytest.mark.parametrize("B,Vx", [(2, 600_000), (1, 2_200_000)])
+def test_long_rows_many_chunks(B, Vx):
+    """Rows of more than 64 chunks (the row merge reads the chunk lists as
+    sorted streams) and of more than 256 (each merging thread owns several
+    streams), with top_k on both sides of the bitonic-tree cut-over."""
+    rng = np.random.default_rng(Vx)
+    x = rng.normal(0, 3, (B, Vx)).astype(np.float32)
+    x[:, rng.choice(Vx, 200, replace=False)] = np.float32(12.5)  # 200 tied ids above the rest
+    for ks in ((64, 20), (50, 47)):
+        params = [sampled(top_k=ks[r % 2], counter=r, top_p=0.95, min_p=0.01) for r in range(B)]
+        check(x, params, tag=f"long rows V={Vx} k={ks}")
+
+
 def test_integer_grid_ties_full_vocab():
     rng = np.random.default_rng(8)
     x = rng.integers(-20, 21, (6, V)).astype(np.float32)
