@@ -390,10 +390,12 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
             a.rows = n;
             int e;
             if (kind == 0) {
-                const int ept = choose_ept(n, V);
+                const bool vec = is_vec_ok(logits, ld);
+                int ept = choose_ept(n, V);
+                if (!vec && ept > 16) ept = 16;  // as for sampling: the scalar-load form spills at 32
                 a.nchunks = (int32_t)chunks_for(V, ept);
                 a.early_xcds = n * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
-                e = rts::launch_logprobs_full(a, ept, is_vec_ok(logits, ld), stream);
+                e = rts::launch_logprobs_full(a, ept, vec, stream);
             } else {
                 e = rts::launch_logprobs_allowed(a, kind == 1 ? fast_lds : bitmap_bytes,
                                                  kind == 2, stream);
@@ -488,11 +490,12 @@ int rts_read_rows(const float *logits, int64_t B, int64_t V, int64_t ld, float *
     const int out_stride = (int)rts::max_chunks(V);
     for (int64_t r0 = 0; r0 < B; r0 += rts::kRowsPerLaunch) {
         const int rows = (int)((B - r0) < rts::kRowsPerLaunch ? (B - r0) : rts::kRowsPerLaunch);
-        const int ept = choose_ept(rows, V);
+        const bool vec = is_vec_ok(logits + r0 * ld, ld);
+        int ept = choose_ept(rows, V);
+        if (!vec && ept > 16) ept = 16;  // the sampler's chunking
         const int nchunks = (int)chunks_for(V, ept);
         const int e = rts::launch_read_rows(logits + r0 * ld, rows, (int)V, ld, nchunks, out_stride,
-                                            chunk_max + r0 * out_stride, ept,
-                                            is_vec_ok(logits + r0 * ld, ld),
+                                            chunk_max + r0 * out_stride, ept, vec,
                                             rows * nchunks <= rts::kEarlyXcdWork, stream);
         if (e != 0) return fail(RTS_EDEVICE, "read launch: %s", hipGetErrorString((hipError_t)e));
     }

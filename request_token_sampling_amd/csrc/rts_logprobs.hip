@@ -411,7 +411,7 @@ int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s)
     case 4: return vec ? launch_full_t<4, true>(a, s) : launch_full_t<4, false>(a, s);
     case 8: return vec ? launch_full_t<8, true>(a, s) : launch_full_t<8, false>(a, s);
     case 16: return vec ? launch_full_t<16, true>(a, s) : launch_full_t<16, false>(a, s);
-    case 32: return vec ? launch_full_t<32, true>(a, s) : launch_full_t<32, false>(a, s);
+    case 32: return vec ? launch_full_t<32, true>(a, s) : (int)hipErrorInvalidValue;  // see the host
     default: return (int)hipErrorInvalidValue;
     }
 }

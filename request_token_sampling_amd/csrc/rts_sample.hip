@@ -240,11 +240,18 @@ static int launch_t(const SampleArgs &a, hipStream_t s)
     return (int)hipGetLastError();
 }
 
+// Rows read element by element (unaligned, or ld % 4 != 0) use at most
+// 4,096-element chunks: the 8,192-element form of that variant spills.
 template <int EPT>
 static int launch_e(const SampleArgs &a, bool vec, hipStream_t s)
 {
-    if (a.lp_on) return vec ? launch_t<EPT, true, true>(a, s) : launch_t<EPT, false, true>(a, s);
-    return vec ? launch_t<EPT, true, false>(a, s) : launch_t<EPT, false, false>(a, s);
+    if constexpr (EPT == 32) {
+        if (!vec) return (int)hipErrorInvalidValue;
+        return a.lp_on ? launch_t<32, true, true>(a, s) : launch_t<32, true, false>(a, s);
+    } else {
+        if (a.lp_on) return vec ? launch_t<EPT, true, true>(a, s) : launch_t<EPT, false, true>(a, s);
+        return vec ? launch_t<EPT, true, false>(a, s) : launch_t<EPT, false, false>(a, s);
+    }
 }
 
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s)
