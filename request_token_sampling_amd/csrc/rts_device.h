@@ -297,6 +297,58 @@ __device__ __forceinline__ uint32_t kth_largest_key_256_q(const uint32_t a[4], i
     return t;
 }
 
+// A lower bound of the k-th largest of the 256 keys a[0..3] of every lane,
+// found over coarser groups: each lane first takes the maximum of its keys in
+// pairs (G = 2) or of all four (G = 1), so the search counts 64 * G group
+// maxima instead of 256 keys.  At least k groups then hold a key >= t, and
+// groups are disjoint, so t is still at most the k-th largest key; it admits a
+// few more candidates, and a step costs G ballots per threshold, not four.
+template <int BITS, int G>
+__device__ __forceinline__ uint32_t kth_largest_group_max(const uint32_t a[4], int k)
+{
+    static_assert(BITS % 2 == 0 && (G == 1 || G == 2 || G == 4), "two bits per step");
+    uint32_t g[G];
+    if constexpr (G == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[i] = a[i];
+    } else if constexpr (G == 2) {
+        g[0] = a[0] > a[1] ? a[0] : a[1];
+        g[1] = a[2] > a[3] ? a[2] : a[3];
+    } else {
+        const uint32_t m0 = a[0] > a[1] ? a[0] : a[1], m1 = a[2] > a[3] ? a[2] : a[3];
+        g[0] = m0 > m1 ? m0 : m1;
+    }
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = 30; b >= 32 - BITS; b -= 2) {
+        const uint32_t c1 = t | (1u << b), c2 = t | (2u << b), c3 = t | (3u << b);
+        int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            n1 += __popcll(__ballot(g[i] >= c1));
+            n2 += __popcll(__ballot(g[i] >= c2));
+            n3 += __popcll(__ballot(g[i] >= c3));
+        }
+        t = (n3 >= k) ? c3 : (n2 >= k) ? c2 : (n1 >= k) ? c1 : t;
+    }
+    return t;
+}
+
+// Selection threshold over 256 lane keys (top 16 bits): the coarsest
+// grouping that keeps the candidates of smooth data within one wave's sort
+// (k <= 24: one group per lane; k <= 40: two).  When fewer than k groups
+// hold a key above that of -inf (sparse chunks, masked rows) the search runs
+// again over all 256 keys, so the degenerate path is taken exactly when the
+// full search would take it.
+__device__ __forceinline__ uint32_t selection_threshold(const uint32_t a[4], int k)
+{
+    uint32_t t;
+    if (k <= 24) t = kth_largest_group_max<16, 1>(a, k);
+    else if (k <= 40) t = kth_largest_group_max<16, 2>(a, k);
+    else return kth_largest_key_256_q<16>(a, k);
+    return t > 0x007FFFFFu ? t : kth_largest_key_256_q<16>(a, k);
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
 // as 1, 2, 3", SC'11): ten rounds of the 4x32 S-box with multipliers

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         const float2 ms = block_max_sum(sm.s, lms.x, lms.y);
         if (tid == 0)
             publish_partial(a.partials + (int64_t)slot * a.partial_stride + chunk, ms);
-        if (raw_sel) raw_done = chunk_compact<EPT>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
+        if (raw_sel) raw_done = chunk_compact<EPT, ToWorkspace, false>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
     }
 
     if (n_eff > 0) {
@@ -184,7 +184,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     }
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    chunk_topk<EPT>(sm.s, v, base, V, k, list + (int64_t)chunk * k, masked);
+    // (the fused variant keeps the full 256-key threshold search: the
+    // grouped one pushes its register peak past 96 and it spills)
+    chunk_topk<EPT, !LP>(sm.s, v, base, V, k, list + (int64_t)chunk * k, masked);
 
     if (raw_sel && !raw_done) {
         __syncthreads();  // the penalised selection's rank may still read sm.part

@@ -175,7 +175,7 @@ __device__ __forceinline__ uint32_t elem_index(int base, int e)
 // above -inf) every id below V is a candidate and v is sanitised in place;
 // with nan_absent, a NaN marks an id outside the row's candidate set (the
 // caller has sanitised the others) and stays excluded.
-template <int EPT, typename Out>
+template <int EPT, typename Out, bool COARSE = true>
 __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], int base, int V,
                                               int k, Cands cd, Out out, bool nan_absent = false)
 {
@@ -216,7 +216,7 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
     if (wave == 0) {
         const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-        const uint32_t t = kth_largest_key_256_q<16>(lk, k);
+        const uint32_t t = COARSE ? selection_threshold(lk, k) : kth_largest_key_256_q<16>(lk, k);
         if (lane == 0) sm.thr = t;
     }
     __syncthreads();
@@ -315,12 +315,12 @@ __device__ __forceinline__ void chunk_finish(SelectSmem &sm, const float (&v)[EP
 // may be raw: NaN stands for -inf and +inf for the largest float, and both
 // are mapped when a key is formed.  Writes the chunk's top-k keys in order to
 // out_keys[0..k) with device-coherent stores.  Ends without a barrier.
-template <int EPT>
+template <int EPT, bool COARSE = true>
 __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int base, int V, int k,
                                            uint64_t *out_keys, bool nan_absent = false)
 {
     const ToWorkspace out{out_keys};
-    if (chunk_compact<EPT>(sm, v, base, V, k, own_cands(sm), out, nan_absent)) return;
+    if (chunk_compact<EPT, ToWorkspace, COARSE>(sm, v, base, V, k, own_cands(sm), out, nan_absent)) return;
     chunk_finish<EPT>(sm, v, base, V, k, own_cands(sm), out, nan_absent);
 }
 
@@ -521,7 +521,7 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
     __syncthreads();
     const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                             sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-    const uint64_t t64 = (uint64_t)kth_largest_key_256_q<16>(lk, k) << 32;
+    const uint64_t t64 = (uint64_t)selection_threshold(lk, k) << 32;
 
     // pass 2: walk every stream while its keys reach the threshold
     const uint64_t below = lanes_below_mask();
