@@ -298,11 +298,11 @@ __device__ __forceinline__ uint32_t kth_largest_key_256_q(const uint32_t a[4], i
 }
 
 // A lower bound of the k-th largest of the 256 keys a[0..3] of every lane,
-// found over coarser groups: each lane first takes the maximum of its keys in
-// pairs (G = 2) or of all four (G = 1), so the search counts 64 * G group
-// maxima instead of 256 keys.  At least k groups then hold a key >= t, and
-// groups are disjoint, so t is still at most the k-th largest key; it admits a
-// few more candidates, and a step costs G ballots per threshold, not four.
+// found over fewer keys: each lane keeps the largest of its four (G = 1) or
+// the two largest (G = 2), so the search counts 64 * G keys instead of 256.
+// At least k of the kept keys are >= t and each is a different lane key, so
+// t is still at most the k-th largest of the 256; it admits a few more
+// candidates, and a step costs G ballots per threshold, not four.
 template <int BITS, int G>
 __device__ __forceinline__ uint32_t kth_largest_group_max(const uint32_t a[4], int k)
 {
@@ -312,8 +312,11 @@ __device__ __forceinline__ uint32_t kth_largest_group_max(const uint32_t a[4], i
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[i] = a[i];
     } else if constexpr (G == 2) {
-        g[0] = a[0] > a[1] ? a[0] : a[1];
-        g[1] = a[2] > a[3] ? a[2] : a[3];
+        const uint32_t h01 = a[0] > a[1] ? a[0] : a[1], l01 = a[0] > a[1] ? a[1] : a[0];
+        const uint32_t h23 = a[2] > a[3] ? a[2] : a[3], l23 = a[2] > a[3] ? a[3] : a[2];
+        g[0] = h01 > h23 ? h01 : h23;
+        const uint32_t m = h01 > h23 ? h23 : h01, l = l01 > l23 ? l01 : l23;
+        g[1] = m > l ? m : l;
     } else {
         const uint32_t m0 = a[0] > a[1] ? a[0] : a[1], m1 = a[2] > a[3] ? a[2] : a[3];
         g[0] = m0 > m1 ? m0 : m1;
@@ -334,18 +337,16 @@ __device__ __forceinline__ uint32_t kth_largest_group_max(const uint32_t a[4], i
     return t;
 }
 
-// Selection threshold over 256 lane keys (top 16 bits): the coarsest
-// grouping that keeps the candidates of smooth data within one wave's sort
-// (k <= 24: one group per lane; k <= 40: two).  When fewer than k groups
-// hold a key above that of -inf (sparse chunks, masked rows) the search runs
-// again over all 256 keys, so the degenerate path is taken exactly when the
-// full search would take it.
+// Selection threshold over 256 lane keys (top 16 bits) from the kept keys
+// above: one per lane for k <= 24, two for larger k (on N(0, 3) rows of
+// 8,192-id chunks this admits 24 candidates at k = 20 and 79 at k = 64,
+// against 21 and 74 for the full search).  When fewer than k kept keys lie
+// above the key of -inf (sparse chunks, masked rows) the search runs again
+// over all 256 keys, so the degenerate path is taken exactly when the full
+// search would take it.
 __device__ __forceinline__ uint32_t selection_threshold(const uint32_t a[4], int k)
 {
-    uint32_t t;
-    if (k <= 24) t = kth_largest_group_max<16, 1>(a, k);
-    else if (k <= 40) t = kth_largest_group_max<16, 2>(a, k);
-    else return kth_largest_key_256_q<16>(a, k);
+    const uint32_t t = k <= 24 ? kth_largest_group_max<16, 1>(a, k) : kth_largest_group_max<16, 2>(a, k);
     return t > 0x007FFFFFu ? t : kth_largest_key_256_q<16>(a, k);
 }
 
