@@ -71,19 +71,22 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     const float y0 = lane_f32(y, 0);
     int m = k > 0 ? 1 : 0, n = m, pick = 0;
     if (!greedy && k > 0) {
-        // The weights are fp64 exponentials of y - y0: untempered for top_p,
-        // tempered for the draw.  Each is computed only where it is used
-        // (top_p < 1; more than one survivor), and a temperature of 1 reuses
-        // the untempered one (dy / 1 is dy exactly).
-        const double dy = (double)y - (double)y0;
-        const bool head_masked = (y0 == -INFINITY);
-        const bool use_top_p = !head_masked && !(R.top_p >= 1.0f);
-        double d = 0.0;
-        if (use_top_p) d = (lane < k) ? exp(dy) : 0.0;
         // min_p: keep the prefix with logit >= head + logf(min_p), in fp32.
         const float thr = y0 + R.lnp;
         m = __popcll(__ballot(lane < k && y >= thr));
         m = m < 1 ? 1 : m;
+        // The weights are fp64 exponentials of y - y0: untempered for top_p,
+        // tempered for the draw.  Each is computed only where it can be used
+        // (top_p < 1; more than one min_p survivor), both before the cuts so
+        // the two chains overlap, and a temperature of 1 reuses the
+        // untempered one (dy / 1 is dy exactly).
+        const double dy = (double)y - (double)y0;
+        const bool head_masked = (y0 == -INFINITY);
+        const bool use_top_p = !head_masked && !(R.top_p >= 1.0f);
+        const bool same_w = use_top_p && R.temperature == 1.0f;
+        double d = 0.0, w = 0.0;
+        if (use_top_p) d = (lane < m) ? exp(dy) : 0.0;
+        if (!head_masked && m > 1 && !same_w) w = (lane < m) ? exp(dy / (double)R.temperature) : 0.0;
         // top_p: shortest prefix of the min_p survivors whose fp64 softmax
         // mass reaches top_p; a masked head (-inf) keeps one candidate.
         n = m;
@@ -99,10 +102,7 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
         const double u = (double)x0 * (1.0 / 4294967296.0);
         pick = n - 1;
         if (n > 1) {
-            const double w = (lane >= n) ? 0.0
-                             : (use_top_p && R.temperature == 1.0f) ? d
-                             : exp(dy / (double)R.temperature);
-            const double S = wave_scan_f64(w);
+            const double S = wave_scan_f64(lane < n ? (same_w ? d : w) : 0.0);
             const double Z = lane_f64(S, n - 1);
             const uint64_t b = __ballot(lane < n - 1 && S / Z > u);
             if (b) pick = __ffsll((unsigned long long)b) - 1;
