@@ -48,6 +48,7 @@ extern "C" {
 #define RTS_KEPT 64      /* entries per row of kept_ids / kept_logits          */
 #define RTS_MAX_TOP_N 20 /* top_logprobs limit (#3200, "Problem and result")   */
 #define RTS_MAX_WINDOW 65535 /* longest penalty window, in ids                  */
+#define RTS_MAX_V (1LL << 30) /* largest vocabulary: ids and chunk offsets stay in 32-bit arithmetic */
 
 /*
  * Per-row request (#19, "What changed": the per-request paragraph lists the
@@ -133,7 +134,7 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * The sampling chain over B rows.
- *   logits      device fp32 [B][ld], row-major, ld >= V; 0 < V < 2^31.  ld = 0
+ *   logits      device fp32 [B][ld], row-major, ld >= V; 0 < V <= 2^30.  ld = 0
  *               makes every row read row 0: several parameter sets (several
  *               samples, a sampled and a greedy pass) over one distribution.
  *   params      host [B].

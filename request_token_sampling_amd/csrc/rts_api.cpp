@@ -171,7 +171,7 @@ int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes)
     clear_error();
     if (bytes == nullptr) return fail(RTS_EINVAL, "bytes is NULL");
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
-    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
     const int64_t rows = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
     *bytes = rts::ws_layout(rows, V).total;
     return RTS_OK;
@@ -202,7 +202,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
     if (B == 0) return RTS_OK;
     if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
-    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
     // ld = 0: every row reads logits row 0 (several parameter sets over one
     // distribution, e.g. several samples of one request)
     if (ld != 0 && ld < V)
@@ -322,7 +322,7 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
     if (B == 0) return RTS_OK;
     if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
-    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
     if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
     if (logits == nullptr || tokens == nullptr || token_lp == nullptr)
         return fail(RTS_EINVAL, "logits, tokens and token_lp must not be NULL");
@@ -483,7 +483,7 @@ int rts_read_rows(const float *logits, int64_t B, int64_t V, int64_t ld, float *
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
     if (B == 0) return RTS_OK;
     if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
-    if (V <= 0 || V >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "V = %lld out of (0, 2^31-1)", (long long)V);
+    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
     if (ld < V) return fail(RTS_EINVAL, "ld = %lld < V = %lld", (long long)ld, (long long)V);
     if (logits == nullptr || chunk_max == nullptr)
         return fail(RTS_EINVAL, "logits and chunk_max must not be NULL");

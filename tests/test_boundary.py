@@ -112,6 +112,9 @@ def test_bad_shapes_and_pointers():
     assert sample(rows, B=-1) == R.RTS_EINVAL
     assert sample(rows, V=0) == R.RTS_EINVAL
     assert sample(rows, V=2**31) == R.RTS_EINVAL
+    assert sample(rows, V=2**30 + 1) == R.RTS_EINVAL and "2^30" in last_error()
+    # the largest vocabulary passes the shape checks (and then needs a larger workspace)
+    assert sample(rows, V=2**30, ld=2**30, ws_bytes=4096) == R.RTS_ENOSPC
     assert sample(rows, ld=999) == R.RTS_EINVAL and "ld" in last_error()
     assert sample(rows, ld=1) == R.RTS_EINVAL and "ld" in last_error()
     assert sample(rows, logits=None) == R.RTS_EINVAL and "logits" in last_error()
