@@ -70,7 +70,7 @@ __device__ __forceinline__ uint64_t lanes_below_mask()
 // 16-lane rows; row_bcast15/31 carry a row's last lane into the next rows.
 // Lanes whose source is out of range or masked off read 0, the identity of
 // the sums and unsigned maxima below.  These stay in the VALU, unlike
-// ds_bpermute-based shuffles.
+// LDS-routed shuffles (ds_bpermute / ds_swizzle).
 // ---------------------------------------------------------------------------
 template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x)
