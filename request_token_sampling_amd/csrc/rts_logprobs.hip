@@ -13,9 +13,11 @@
 // keys (rts_select.h), and publishes one (max, sum) pair and K keys.  The
 // last workgroup of the row combines the pairs in fp64 in chunk order and
 // merges the keys.
-// Restricted rows: one workgroup per row marks the named ids in an LDS bitmap
-// of the vocabulary (duplicates collapse), then walks the set bits, so each
-// member is gathered exactly once.
+// Restricted rows: one workgroup per row and an LDS bitmap of the vocabulary,
+// so duplicates count once and foreign ids are ignored.  Lists of up to
+// kAllowedFast ids are gathered at once into registers, the thread that sets
+// an id's bit owning it; longer lists are marked first and the set bits
+// walked, so each member is gathered exactly once.
 #include "rts_select.h"
 
 namespace rts {
