@@ -33,6 +33,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // The chunk at `base` into registers, element e of the thread at
 // elem_index(base, e); ids past V (only in the last chunk) read as NaN.
+// The 16-byte loads carry the nontemporal hint (the `nt` bit): the logits
+// are streamed once, and on MI355X this measured 2-3 % faster on 40 rows and
+// on one row read as two broadcast parameter rows (ld = 0), whose second
+// reads still find the chunk in the XCD's L2.
 template <int EPT, bool VEC>
 __device__ __forceinline__ void load_chunk(const float *x, int base, int V, float (&v)[EPT])
 {
@@ -41,7 +45,7 @@ __device__ __forceinline__ void load_chunk(const float *x, int base, int V, floa
     for (int q = 0; q < EPT / 4; ++q) {
         const int i0 = base + q * 1024 + tid * 4;
         if (VEC && i0 + 4 <= V) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(x + i0);
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + i0));
             v[4 * q + 0] = t.x;
             v[4 * q + 1] = t.y;
             v[4 * q + 2] = t.z;
