@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void logprob_kernel(const
     for (int q = 0; q < NQ; ++q) {
         const int i0 = base + q * 1024 + tid * 4;
         if (VEC && i0 + 4 <= V) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(x + i0);
+            // streamed once: the nontemporal hint, as in the sampler
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + i0));
             v[4 * q + 0] = t.x;
             v[4 * q + 1] = t.y;
             v[4 * q + 2] = t.z;
