@@ -145,3 +145,47 @@ def test_windows_with_masks_and_device_counters_repeat():
         exp = O.accept_windows(om["token"], window, drafts)
         if np.array_equal(g["token"], om["token"]):
             assert np.array_equal(g["accepted"], exp)
+
+
+def test_graph_replays_of_windows_masks_and_fused_logprobs():
+    """One captured call with every feature at once -- two launches (70 rows
+    in windows of 5), masks on two rows, fused logprobs, device counters --
+    replayed three times with eager work between replays: each replay draws
+    with the advanced counters and the self-resetting tickets (row, logprob
+    and window) start from zero every time."""
+    B, window, top_n = 70, 5, 20
+    x, params, _, drafts = windows_case(B, window, 91)
+    lists = [None] * B
+    lists[3] = np.arange(0, V, 11, dtype=np.int32)
+    lists[64] = np.array([5, 17, 17, 123456, V - 1, -4, V + 9], np.int32)
+    ids, off = W.pack_allowed(lists)
+    xd = to_dev(x)
+    c0 = np.array([p["counter"] for p in params], np.int64)
+    ctr = to_dev(c0)
+    call = R.SampleCall(xd, params, counters=ctr, counter_stride=1, logprobs=top_n,
+                        window=window, draft=to_dev(drafts), allowed=to_dev(ids), allowed_off=off)
+    call()                                     # eager warm-up: loads the kernels
+    torch.cuda.synchronize()
+    ctr.copy_(to_dev(c0))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("case graph replay, all features", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        g = {k: v.cpu().numpy().copy() for k, v in call.results().items()}
+        want = [dict(p, counter=int(c0[r]) + rep) for r, p in enumerate(params)]
+        om = O.sample_tokens_masked(x, want, lists)
+        compare_sample(g, om, f"graph replay {rep}")
+        compare_fused_logprobs(g, om, x, top_n, f"graph replay {rep} logprobs")
+        exp = O.accept_windows(om["token"], window, drafts)
+        for w in range(B // window):
+            rows = slice(w * window, (w + 1) * window)
+            if np.array_equal(g["token"][rows], om["token"][rows]):
+                assert g["accepted"][w] == exp[w], (rep, w)
+        float((xd * 2.0).sum().item())         # eager work between replays
+        torch.cuda.synchronize()
+    assert np.array_equal(ctr.cpu().numpy(), c0 + 3)
