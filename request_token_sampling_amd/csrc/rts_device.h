@@ -259,25 +259,10 @@ __device__ __forceinline__ void wave_sort_desc(uint64_t &x0, uint64_t &x1)
     }
 }
 
-// Largest t (to `bits` leading bits) with #{keys >= t} >= k, over the four
-// keys a[0..3] held by each lane of the wave (256 keys).  Every wave that runs
-// this on the same keys gets the same t, so no broadcast is needed.
-template <int BITS>
-__device__ __forceinline__ uint32_t kth_largest_key_256(const uint32_t a[4], int k)
-{
-    uint32_t t = 0;
-#pragma unroll
-    for (int b = 31; b >= 32 - BITS; --b) {
-        const uint32_t c = t | (1u << b);
-        const int cnt = __popcll(__ballot(a[0] >= c)) + __popcll(__ballot(a[1] >= c)) +
-                        __popcll(__ballot(a[2] >= c)) + __popcll(__ballot(a[3] >= c));
-        if (cnt >= k) t = c;
-    }
-    return t;
-}
-
-// The same t, two bits per step: the three thresholds of a step are counted
-// together, so the dependent chain is half as long.
+// Largest t (to BITS leading bits) with #{keys >= t} >= k, over the four
+// keys a[0..3] held by each lane of the wave (256 keys), settled two bits per
+// step: the three thresholds of a step are counted together.  Every wave that
+// runs this on the same keys gets the same t, so no broadcast is needed.
 template <int BITS>
 __device__ __forceinline__ uint32_t kth_largest_key_256_q(const uint32_t a[4], int k)
 {

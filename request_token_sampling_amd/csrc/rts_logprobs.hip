@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_wide_kernel(const Logp
         __syncthreads();
         const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-        const float tf = key_threshold(kth_largest_key_256<32>(lk, K));
+        const float tf = key_threshold(selection_threshold(lk, K));
         for (int w = tid; w < nw; w += kBlock) {
             uint32_t bits = bm[w];
             while (bits) {
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kBlock) void logprob_allowed_kernel(const LogprobAr
         __syncthreads();
         const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-        const float tf = key_threshold(kth_largest_key_256<16>(lk, K));
+        const float tf = key_threshold(selection_threshold(lk, K));
         const uint64_t below = lanes_below_mask();
         uint64_t *wc = sm.cand + wave * kRegion;
         uint32_t wcnt = 0;
