@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="single_stream",
                     choices=["single_stream", "window", "batch", "stress"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm (same-buffer) figure, so every sampler launch of the run "
+                         "reads cold rows (used for the rocprofv3 kernel averages)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads' figures in the JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -334,10 +337,10 @@ def time_alt_graph(wl, steps):
     return wall / steps
 
 
-def measure(wl, steps, warmup):
+def measure(wl, steps, warmup, warm=True):
     eager = time_eager(wl, steps, warmup)
     graph = time_graph(wl, steps)
-    warm = time_graph(wl, steps, warm=True)
+    warm = time_graph(wl, steps, warm=True) if warm else None
     kern = kernel_durations(wl, min(steps, 500))
     alt = time_alt_graph(wl, steps) if wl.alt_calls else None
     return dict(graph_wall=graph, warm_wall=warm, eager_wall=eager, kern_ms=kern,
@@ -517,7 +520,7 @@ def main():
         calibration_copy(dev)
     wl = Workload(args.workload, dev)
     progress(f"{args.workload}: {wl.ncopies} copies resident, timing {args.steps} steps")
-    m = measure(wl, args.steps, args.warmup)
+    m = measure(wl, args.steps, args.warmup, warm=not args.no_warm)
     progress(f"{args.workload}: graph {m['graph_wall'] / args.steps * 1e3:.4f} ms/step, eager "
              f"{m['eager_wall'] / args.steps * 1e3:.4f} ms/step, kernels {m['kern_ms']}")
     value = wl.sampled_rows * args.steps / m["graph_wall"]
@@ -541,10 +544,12 @@ def main():
         "roofline": dict(roofline(wl, m["kern_ms"]), read_floor=m["floor"]),
         "eager": {"value": round(wl.sampled_rows * args.steps / m["eager_wall"], 1),
                   "ms_per_step": round(m["eager_wall"] / args.steps * 1e3, 5)},
-        "warm": {"value": round(wl.sampled_rows * args.steps / m["warm_wall"], 1),
-                 "ms_per_step": round(m["warm_wall"] / args.steps * 1e3, 5),
-                 "note": "every step reads the same logits copy (cache-resident); context only"},
     }
+    if m["warm_wall"] is not None:
+        line["warm"] = {"value": round(wl.sampled_rows * args.steps / m["warm_wall"], 1),
+                        "ms_per_step": round(m["warm_wall"] / args.steps * 1e3, 5),
+                        "note": "every step reads the same logits copy (cache-resident); "
+                                "context only"}
     if m["alt"] is not None:
         line["separate_launches"] = {"value": round(wl.sampled_rows / m["alt"], 1),
                                      "ms_per_step": round(m["alt"] * 1e3, 5),
@@ -556,14 +561,15 @@ def main():
                 continue
             w2 = Workload(name, dev)
             steps = max(50, args.steps // 4)
-            m2 = measure(w2, steps, max(10, args.warmup // 4))
+            m2 = measure(w2, steps, max(10, args.warmup // 4), warm=not args.no_warm)
             progress(f"{name}: graph {m2['graph_wall'] / steps * 1e3:.4f} ms/step, kernels "
                      f"{m2['kern_ms']}")
             extra[name] = dict(value=round(w2.sampled_rows * steps / m2["graph_wall"], 1),
                                unit="rows/s", steps=steps,
                                ms_per_step=round(m2["graph_wall"] / steps * 1e3, 5),
                                eager_ms_per_step=round(m2["eager_wall"] / steps * 1e3, 5),
-                               warm_ms_per_step=round(m2["warm_wall"] / steps * 1e3, 5),
+                               warm_ms_per_step=(None if m2["warm_wall"] is None
+                                                 else round(m2["warm_wall"] / steps * 1e3, 5)),
                                roofline=dict(roofline(w2, m2["kern_ms"]), read_floor=m2["floor"]),
                                desc=w2.desc,
                                passes_per_step=w2.passes)
