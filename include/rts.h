@@ -25,7 +25,8 @@
  *    rts_last_error() names the offending row and field (per thread).
  *  - Device-resident ids (history rows, allowed lists, tokens) are not
  *    validated: ids outside [0, V) are ignored as the pages' semantics
- *    require no host round trip.
+ *    require no host round trip (rts_sample_extras.ignored_ids counts the
+ *    ones a sampling call ignored).
  */
 #ifndef RTS_H
 #define RTS_H
@@ -113,6 +114,13 @@ typedef struct rts_logprob_request {
  *               are 0.  The fused logprobs stay unrestricted.
  *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] >= 0,
  *               allowed_off[B] < 2^31.
+ *   ignored_ids device uint32 [1], or NULL.  The call adds the number of
+ *               device-resident ids it read and ignored because they lie
+ *               outside [0, V): history ids in the window of a row whose
+ *               penalties apply, and allowed ids of masked rows, each
+ *               occurrence once per row.  Ids are not validated otherwise
+ *               (that would need a host round trip); this word lets a
+ *               caller notice bad ids without one.
  */
 typedef struct rts_sample_extras {
     int32_t window;
@@ -121,6 +129,7 @@ typedef struct rts_sample_extras {
     int32_t *accepted;
     const int32_t *allowed;
     const int64_t *allowed_off;
+    uint32_t *ignored_ids;
 } rts_sample_extras;
 
 /* Bytes of workspace that calls with up to B rows of V logits need

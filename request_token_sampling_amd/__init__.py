@@ -77,10 +77,11 @@ class SampleExtras(ctypes.Structure):
         ("accepted", ctypes.c_void_p),
         ("allowed", ctypes.c_void_p),
         ("allowed_off", ctypes.c_void_p),
+        ("ignored_ids", ctypes.c_void_p),
     ]
 
 
-assert ctypes.sizeof(SampleExtras) == 40
+assert ctypes.sizeof(SampleExtras) == 48
 
 _DEFAULTS = dict(temperature=0.0, top_k=0, top_p=1.0, min_p=0.0, penalty_repeat=1.0,
                  penalty_freq=0.0, penalty_present=0.0, penalty_last_n=0, history_row=-1,
@@ -173,7 +174,7 @@ class SampleCall:
 
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
                  stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
-                 draft=None, allowed=None, allowed_off=None):
+                 draft=None, allowed=None, allowed_off=None, ignored=None):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -208,7 +209,10 @@ class SampleCall:
         # verify windows (window rows each, drafts per row) and allowed-id masks
         self.ex = None
         self.accepted = None
-        if window or allowed is not None:
+        if ignored is not None and (ignored.dtype != torch.int32 or not ignored.is_cuda):
+            raise ValueError("ignored must be a CUDA int32 tensor (one counter word)")
+        self.ignored = ignored
+        if window or allowed is not None or ignored is not None:
             if window:
                 if draft is None or draft.dtype != torch.int32 or not draft.is_cuda:
                     raise ValueError("window needs draft: a CUDA int32 tensor of B ids")
@@ -222,7 +226,8 @@ class SampleCall:
                                    None if self.accepted is None else self.accepted.data_ptr(),
                                    None if allowed is None else allowed.data_ptr(),
                                    None if allowed is None
-                                   else self.allowed_off.ctypes.data_as(ctypes.c_void_p))
+                                   else self.allowed_off.ctypes.data_as(ctypes.c_void_p),
+                                   None if ignored is None else ignored.data_ptr())
         self.set_params(params)
         self.stream = stream
 
@@ -263,7 +268,7 @@ class SampleCall:
 
 def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
                   stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
-                  draft=None, allowed=None, allowed_off=None) -> dict:
+                  draft=None, allowed=None, allowed_off=None, ignored=None) -> dict:
     """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
 
     params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
@@ -277,9 +282,12 @@ def sample_tokens(logits, params, history=None, history_len=None, workspace=None
     window, draft: verify windows of `window` rows with a CUDA int32 draft id
     per row; adds accepted[B / window], the tokens each window emits.
     allowed, allowed_off: CUDA int32 ids with host int64 offsets [B+1]; a row
-    with a non-empty list samples only among those ids."""
+    with a non-empty list samples only among those ids.
+    ignored: optional CUDA int32 [1] counter; the call adds the number of
+    device ids it read and ignored (outside [0, V))."""
     return SampleCall(logits, params, history, history_len, workspace, stream, counters,
-                      counter_stride, logprobs, window, draft, allowed, allowed_off)().results()
+                      counter_stride, logprobs, window, draft, allowed, allowed_off,
+                      ignored)().results()
 
 
 class LogprobCall:

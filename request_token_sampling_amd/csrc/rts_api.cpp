@@ -283,6 +283,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         a.chunk_major = (ld == 0 && rows > 1) ? 1 : 0;
         a.early_xcds = rts::sample_work(rows, a.nchunks, 1, a.chunk_major) <= rts::kEarlyXcdWork ? 1 : 0;
         a.allowed = allowed;
+        a.ignored = ex ? ex->ignored_ids : nullptr;
         if (window > 0) {
             a.window = window;
             a.draft = ex->draft + r0;

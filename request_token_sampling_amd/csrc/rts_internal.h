@@ -107,6 +107,7 @@ struct SampleArgs {
     const int32_t *draft;    // verify windows: draft id per row, row 0 of this launch
     int32_t *accepted;       // tokens emitted per window, window 0 of this launch
     uint32_t *wtickets;      // workspace: one ticket per window slot
+    uint32_t *ignored;       // device count of ids read and ignored (outside [0, V)), or NULL
     int32_t window;          // rows per verify window; 0: none
     int32_t chunk_major;     // 1: rows share one logits row; a chunk's rows share an XCD
     SampleRow row[kRowsPerLaunch];

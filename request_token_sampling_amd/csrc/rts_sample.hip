@@ -124,15 +124,21 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         if (raw_sel) raw_done = chunk_compact<EPT, ToWorkspace, false>(sm.s, v, base, V, K, rawc, ToWorkspace{raw_out});
     }
 
+    // Ids read and ignored (outside [0, V)) are counted by each row's
+    // chunk-0 workgroup, when the caller asks for the count.
+    const bool count_ignored = a.ignored != nullptr && chunk == 0;
     if (n_eff > 0) {
         // Clear the chunk's bits and only the count words the window touches.
         for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
         const int32_t *h = a.history + R.hist_off;
+        uint32_t bad = 0;
         for (int j = tid; j < n_eff; j += kBlock) {
             const int32_t id = h[j];
             const int rel = id - base;
             if (id >= 0 && id < V && rel >= 0 && rel < CH) sm.pen_cnt[rel >> 1] = 0u;
+            bad += (id < 0 || id >= V) ? 1u : 0u;
         }
+        if (count_ignored && bad) atomicAdd(a.ignored, bad);
         __syncthreads();
         for (int j = tid; j < n_eff; j += kBlock) {
             const int32_t id = h[j];
@@ -170,12 +176,15 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
         __syncthreads();
         const int32_t *al = a.allowed + R.allowed_off;
+        uint32_t bad = 0;
         for (int j = tid; j < R.allowed_cnt; j += kBlock) {
             const int32_t id = al[j];
             const int rel = id - base;
             if (id >= 0 && id < V && rel >= 0 && rel < CH)
                 atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
+            bad += (id < 0 || id >= V) ? 1u : 0u;
         }
+        if (count_ignored && bad) atomicAdd(a.ignored, bad);
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {

@@ -48,6 +48,10 @@ def test_struct_layout_matches_header():
     fields = re.findall(r"^\s*(?:float|int32_t)\s*\*?\s*(\w+);", body, flags=re.M)
     assert fields == [f for f, _ in R.LogprobRequest._fields_]
     assert ctypes.sizeof(R.LogprobRequest) == 32
+    body = text[text.index("typedef struct rts_sample_extras"):text.index("} rts_sample_extras;")]
+    fields = re.findall(r"^\s*(?:const\s+)?(?:int32_t|int64_t|uint32_t)\s*\*?\s*(\w+);", body, flags=re.M)
+    assert fields == [f for f, _ in R.SampleExtras._fields_]
+    assert ctypes.sizeof(R.SampleExtras) == 48
 
 
 def sample(params, B=None, V=1000, ld=None, logits=FAKE, token=FAKE, ws=FAKE, ws_bytes=BIG_WS,

@@ -224,6 +224,44 @@ def test_penalty_windows_and_foreign_ids():
     check(x, params, hist, hist_len, tag="penalty windows")
 
 
+def test_ignored_ids_are_counted():
+    """The optional status word counts the device ids a call read and
+    ignored: history ids outside [0, V) inside the windows of rows whose
+    penalties apply, and allowed ids outside [0, V) of masked rows, once
+    per occurrence and row; outputs equal the same call without it."""
+    rng = np.random.default_rng(12)
+    Vx = 50000
+    hist = rng.integers(0, 2000, (2, 300)).astype(np.int32)
+    hist[0, 250:262] = [-1, Vx, Vx + 5, 2**31 - 1, -7, Vx] * 2     # 12 bad ids, last 64 window
+    hist[1, :20] = [-3, Vx] * 10                                    # 20 bad, outside an 8-id window
+    hist_len = [300, 300]
+    x = rng.normal(0, 2, (5, Vx)).astype(np.float32)
+    params = [
+        sampled(top_k=20, penalty_repeat=1.3, penalty_last_n=64, history_row=0),
+        sampled(top_k=20, penalty_repeat=1.3, penalty_last_n=-1, history_row=1, counter=1),
+        sampled(top_k=20, penalty_last_n=-1, history_row=0, counter=2),  # neutral: not read
+        sampled(top_k=20, penalty_repeat=1.1, penalty_last_n=8, history_row=1, counter=3),
+        sampled(top_k=20, counter=4),                                   # masked below
+    ]
+    lists = [None, None, None, None, np.array([5, -1, Vx, 17, Vx + 1, 40000], np.int32)]
+    ids, off = W.pack_allowed(lists)
+    # rows 0 and 1 read 12 and 20 bad history ids (row 3's window holds none);
+    # row 4 reads 3 bad allowed ids
+    expected = 12 + 20 + 3
+    xd, hd, idd = to_dev(x), to_dev(hist), to_dev(ids)
+    say("case ignored ids", expected)
+    ign = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = R.sample_tokens(xd, params, hd, hist_len, allowed=idd, allowed_off=off, ignored=ign)
+    ref = R.sample_tokens(xd, params, hd, hist_len, allowed=idd, allowed_off=off)
+    torch.cuda.synchronize()
+    assert int(ign.item()) == expected
+    for k in out:
+        assert torch.equal(out[k], ref[k]), k
+    R.sample_tokens(xd, params, hd, hist_len, allowed=idd, allowed_off=off, ignored=ign)
+    torch.cuda.synchronize()
+    assert int(ign.item()) == 2 * expected        # the word accumulates over calls
+
+
 def test_determinism_and_row_independence():
     w = W.batch_slots()
     x, p = w["logits"], w["params"]
