@@ -435,16 +435,19 @@ __device__ __forceinline__ void tree_topk(SelectSmem &sm, const uint64_t *list, 
 // are the top ranks of every chunk; the k-th largest of them is then close to
 // the row's k-th key.  With more chunks each lane owns whole chunks t, t + 256,
 // ...  A lane stops reading a stream at its first key below the threshold.
-// Loads are device-coherent and issued kBatch (four) at a time: a stream of
-// a 20-key list over 31 chunks holds 3 keys, so one batch covers it, and a
-// shorter batch leaves fewer empty compaction steps (8 measured 2-3 % slower
-// on one row and on a 5-row window).  The threshold is a
+// Loads are device-coherent and issued kBatch (two) at a time.  Past the
+// threshold a stream rarely keeps more than its head (a 20-key list over 31
+// chunks has 3 keys per stream, ~23 of the 620 survive), so short batches
+// leave few empty compaction steps; a stream that does continue costs one
+// more round trip per batch (measured on MI355X: batches of 2 against 4,
+// 1-row step -1 %, 5-row window -3.5 %; 4 against 8, -2.5 % and -2 %).
+// The threshold is a
 // lower bound from selection_threshold, so a few more keys than k survive.
 // For k >= kTreeMinK with at most kTreeMaxLists chunks the bitonic tree above
 // merges the lists instead.  On return sm.sel is valid in wave 0 (in every
 // wave only when the call ended with a barrier, which callers must not rely
 // on).
-constexpr int kBatch = 4;
+constexpr int kBatch = 2;
 
 struct MergeStreams {
     int G;        // rank stride inside a stream
