@@ -324,109 +324,6 @@ __device__ __forceinline__ void chunk_topk(SelectSmem &sm, float (&v)[EPT], int 
     chunk_finish<EPT>(sm, v, base, V, k, own_cands(sm), out, nan_absent);
 }
 
-// ---------------------------------------------------------------------------
-// Row merge by a bitonic tree (rows of at most 64 chunks).  A chunk list is
-// held as one key per lane, in descending or ascending lane order (zero keys
-// past the list's k entries).  The lane-wise maximum of a descending and an
-// ascending run holds the 64 largest keys of both and is bitonic (Batcher's
-// half-cleaner), so six more half-cleaner steps sort it, in either order.
-// Merging the lists pairwise in a binary tree, left children descending and
-// right children ascending, leaves the row's top 64 sorted at the root.
-// ---------------------------------------------------------------------------
-// The tree's cost does not depend on k while the threshold path's grows with
-// it; measured on MI355X (31 chunk lists of a 248,320-id row) the tree is
-// faster from k = 48 on, slower at k <= 40.
-constexpr int kTreeMaxLists = 64;
-constexpr int kTreeMinK = 48;
-
-template <int J>
-__device__ __forceinline__ uint64_t bitonic_clean(uint64_t x, bool desc)
-{
-    const bool lower = (lane_id() & J) == 0;
-    x = keep(x, xor_lane_u64<J>(x), lower == desc);
-    if constexpr (J > 1) return bitonic_clean<J / 2>(x, desc);
-    return x;
-}
-
-__device__ __forceinline__ uint64_t merge_top64(uint64_t a_desc, uint64_t b_asc, bool desc)
-{
-    return bitonic_clean<32>(a_desc > b_asc ? a_desc : b_asc, desc);
-}
-
-// Chunk c's list as a leaf: lane l holds entry l (descending) or 63 - l
-// (ascending); entries at or past k, and lists at or past C, read as zero.
-__device__ __forceinline__ uint64_t load_leaf(const uint64_t *list, int C, int k, int c, bool desc)
-{
-    const int lane = lane_id();
-    const int e = desc ? lane : 63 - lane;
-    return (c < C && e < k) ? read_published_u64(list + (int64_t)c * k + e) : 0ull;
-}
-
-// Merge N leaves held in x (leaf j descending for even j, ascending for odd
-// j) into one run in the requested order.
-template <int N>
-__device__ __forceinline__ uint64_t tree_merge(uint64_t (&x)[N], bool desc)
-{
-#pragma unroll
-    for (int w = N; w > 1; w /= 2) {
-#pragma unroll
-        for (int m = 0; m < w / 2; ++m)
-            x[m] = merge_top64(x[2 * m], x[2 * m + 1], (w == 2) ? desc : ((m & 1) == 0));
-    }
-    return x[0];
-}
-
-// Each wave merges N consecutive lists (wave w: lists wN .. wN + N - 1) into
-// one run, descending for even waves and ascending for odd ones; the first
-// loads are in flight when `overlap` runs.
-template <int N, typename Overlap>
-__device__ __forceinline__ uint64_t wave_subtree(const uint64_t *list, int C, int k, int first,
-                                                 bool desc, Overlap &overlap)
-{
-    uint64_t x[N];
-#pragma unroll
-    for (int j = 0; j < N; ++j) x[j] = load_leaf(list, C, k, first + j, N == 1 ? desc : (j & 1) == 0);
-    overlap();
-    return tree_merge<N>(x, desc);
-}
-
-// Top-k of C <= 64 chunk lists into sm.sel[0..k) (valid in wave 0 on return).
-template <typename Overlap>
-__device__ __forceinline__ void tree_topk(SelectSmem &sm, const uint64_t *list, int C, int k,
-                                          Overlap &overlap)
-{
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    uint64_t r;
-    if (C <= 2) {
-        // one wave merges everything
-        if (wave != 0) return;
-        if (C == 1) r = wave_subtree<1>(list, C, k, 0, true, overlap);
-        else r = wave_subtree<2>(list, C, k, 0, true, overlap);
-    } else {
-        const int L = C <= 4 ? 4 : C <= 8 ? 8 : C <= 16 ? 16 : C <= 32 ? 32 : 64;
-        const int N = L / 4;
-        const bool desc = (wave & 1) == 0;
-        switch (N) {
-        case 1: r = wave_subtree<1>(list, C, k, wave, desc, overlap); break;
-        case 2: r = wave_subtree<2>(list, C, k, 2 * wave, desc, overlap); break;
-        case 4: r = wave_subtree<4>(list, C, k, 4 * wave, desc, overlap); break;
-        case 8: r = wave_subtree<8>(list, C, k, 8 * wave, desc, overlap); break;
-        default: r = wave_subtree<16>(list, C, k, 16 * wave, desc, overlap); break;
-        }
-        // waves 1-3 hand their runs to wave 0, which merges the four
-        if (wave != 0) sm.cand[(wave - 1) * 64 + lane] = r;
-        __syncthreads();
-        if (wave != 0) return;
-        const uint64_t a = merge_top64(r, sm.cand[lane], true);
-        const uint64_t b = merge_top64(sm.cand[64 + lane], sm.cand[128 + lane], false);
-        r = merge_top64(a, b, true);
-    }
-    if (lane < k) sm.sel[lane] = r;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Row merge: top-k of the chunk lists, written in order to sm.sel[0..k).
 // Chunk c published its top-k keys in descending order at list[c*k ..
 // c*k + k), zero-padded.  The lists are read as sorted streams: with C <= 256
@@ -443,10 +340,8 @@ __device__ __forceinline__ void tree_topk(SelectSmem &sm, const uint64_t *list, 
 // 1-row step -1 %, 5-row window -3.5 %; 4 against 8, -2.5 % and -2 %).
 // The threshold is a
 // lower bound from selection_threshold, so a few more keys than k survive.
-// For k >= kTreeMinK with at most kTreeMaxLists chunks the bitonic tree above
-// merges the lists instead.  On return sm.sel is valid in wave 0 (in every
-// wave only when the call ended with a barrier, which callers must not rely
-// on).
+// On return sm.sel is valid in wave 0 (in every wave only when the call
+// ended with a barrier, which callers must not rely on).
 constexpr int kBatch = 2;
 
 struct MergeStreams {
@@ -502,10 +397,6 @@ __device__ __forceinline__ void list_topk(SelectSmem &sm, const uint64_t *list, 
                                           Overlap overlap = NoWork{})
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    if (k >= kTreeMinK && C <= kTreeMaxLists) {
-        tree_topk(sm, list, C, k, overlap);
-        return;
-    }
     const MergeStreams ms = merge_streams(C, k);
 
     // pass 1: the first batch of the first stream (kept), heads of the others
