@@ -1,0 +1,104 @@
+"""Seeded random configurations through the whole call surface at once:
+random B, V, logit distributions (normal, integer ties, bf16 grids, special
+values), per-row parameters (greedy and sampled, penalties over random
+windows with foreign ids, masks), fused logprobs, broadcast rows (ld = 0) and
+device counters, each against the oracle (page "#19 serve: per-request
+temperature/top_p/top_k/min_p/penalties sampling", "What changed"; page
+"#3200 [Engine] OpenAI logprobs / top_logprobs / allowed_token_ids for the
+CUDA/HIP engine", "Approach")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.oracle as O
+import request_token_sampling_amd as R
+from request_token_sampling_amd import workloads as W
+
+from parity import compare_fused_logprobs, compare_sample, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _logits(rng, B, V):
+    kind = rng.integers(0, 4)
+    if kind == 0:
+        x = rng.normal(0, rng.uniform(0.5, 4), (B, V))
+    elif kind == 1:
+        x = rng.integers(-8, 9, (B, V))
+    elif kind == 2:
+        x = rng.normal(0, 3, (B, V)).astype(np.float32)
+        x = (x.view(np.uint32) & 0xFFFF0000).view(np.float32)
+    else:
+        x = rng.normal(0, 2, (B, V))
+        for r in range(B):
+            pos = rng.choice(V, min(V, 12), replace=False)
+            x[r, pos[:3]] = np.nan
+            x[r, pos[3:5]] = np.inf
+            x[r, pos[5:8]] = -np.inf
+    return np.asarray(x, np.float32), int(kind)
+
+
+def _params(rng, B, H, V):
+    out = []
+    for r in range(B):
+        if rng.random() < 0.2:
+            p = W.row_params()
+        else:
+            p = W.row_params(temperature=float(rng.uniform(0.1, 2.0)), top_k=int(rng.integers(1, 65)),
+                             top_p=float(rng.uniform(0.3, 1.0)) if rng.random() < 0.7 else 1.0,
+                             min_p=float(rng.uniform(0, 0.3)) if rng.random() < 0.5 else 0.0,
+                             seed=int(rng.integers(0, 1 << 62)), counter=int(rng.integers(0, 1 << 40)))
+        if H and rng.random() < 0.5:
+            p.update(penalty_repeat=float(rng.uniform(0.7, 1.6)),
+                     penalty_freq=float(rng.uniform(-0.3, 0.6)),
+                     penalty_present=float(rng.uniform(-0.3, 0.6)),
+                     penalty_last_n=int(rng.choice([-1, 0, 1, 8, 64, 300])),
+                     history_row=int(rng.integers(0, H)))
+        out.append(p)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configuration(seed):
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.choice([1, 2, 3, 5, 17, 40, 70]))
+    V = int(rng.choice([1, 7, 100, 1023, 4097, 30011, 65536, 120000]))
+    broadcast = B > 1 and rng.random() < 0.25
+    x, kind = _logits(rng, 1 if broadcast else B, V)
+    xs = np.repeat(x, B, axis=0) if broadcast else x
+    H = int(rng.integers(0, 3))
+    hist = rng.integers(-2, V + 2, (H, 200)).astype(np.int32) if H else None
+    hist_len = [int(rng.integers(0, 201)) for _ in range(H)] if H else None
+    params = _params(rng, B, H, V)
+    masked = rng.random() < 0.3
+    lists = [None] * B
+    if masked:
+        for r in range(B):
+            if rng.random() < 0.5:
+                lists[r] = rng.integers(-3, V + 3, int(rng.integers(0, 40))).astype(np.int32)
+    top_n = int(rng.choice([0, 1, 5, 20])) if rng.random() < 0.5 else None
+    say("case random", seed, dict(B=B, V=V, kind=kind, broadcast=broadcast, H=H, masked=masked,
+                                  top_n=top_n))
+
+    xd = to_dev(x)
+    view = xd.expand(B, -1) if broadcast else xd
+    hd = None if hist is None else to_dev(hist)
+    ctr = to_dev(np.array([p["counter"] for p in params], np.int64))
+    kw = {}
+    if masked:
+        ids, off = W.pack_allowed(lists)
+        kw = dict(allowed=to_dev(ids) if ids.size else torch.zeros(1, dtype=torch.int32,
+                                                                     device="cuda"),
+                  allowed_off=off)
+    out = R.sample_tokens(view, params, hd, hist_len, counters=ctr, counter_stride=3,
+                          logprobs=top_n, **kw)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    if masked:
+        o = O.sample_tokens_masked(xs, params, lists, hist, hist_len)
+    else:
+        o = O.sample_tokens(xs, params, hist, hist_len)
+    compare_sample(g, o, f"random {seed}")
+    if top_n is not None:
+        compare_fused_logprobs(g, o, xs, top_n, f"random {seed} logprobs")
+    assert np.array_equal(ctr.cpu().numpy(), [p["counter"] + 3 for p in params])
