@@ -14,7 +14,7 @@ import oracle.oracle as O
 import request_token_sampling_amd as R
 from request_token_sampling_amd import workloads as W
 
-from parity import compare_fused_logprobs, compare_sample, say, to_dev
+from parity import compare_fused_logprobs, compare_logprobs, compare_sample, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -102,3 +102,43 @@ def test_random_configuration(seed):
     if top_n is not None:
         compare_fused_logprobs(g, o, xs, top_n, f"random {seed} logprobs")
     assert np.array_equal(ctr.cpu().numpy(), [p["counter"] + 3 for p in params])
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_logprob_configuration(seed):
+    """rts_token_logprobs on seeded random inputs: unrestricted rows, short
+    allowed lists (gathered into registers) and long ones (walked in the
+    bitmap), duplicates, foreign ids and out-of-range tokens."""
+    rng = np.random.default_rng(9000 + seed)
+    B = int(rng.choice([1, 3, 17, 40, 70]))
+    V = int(rng.choice([1, 9, 1000, 4097, 30011, 120000]))
+    x, kind = _logits(rng, B, V)
+    top_n = int(rng.choice([0, 1, 7, 20]))
+    tokens = rng.integers(-2, V + 2, B).astype(np.int32)
+    lists = None
+    if rng.random() < 0.6:
+        lists = []
+        for r in range(B):
+            u = rng.random()
+            if u < 0.3:
+                lists.append(None)
+            elif u < 0.8:
+                lists.append(rng.integers(-3, V + 3, int(rng.integers(0, 300))).astype(np.int32))
+            else:
+                lists.append(rng.integers(-3, V + 3, int(rng.integers(4097, 6000))).astype(np.int32))
+            if lists[-1] is not None and lists[-1].size and rng.random() < 0.5:
+                tokens[r] = lists[-1][0]            # a listed token (maybe foreign)
+    say("case random logprobs", seed, dict(B=B, V=V, kind=kind, top_n=top_n,
+                                           allowed=lists is not None))
+    xd = to_dev(x)
+    t = to_dev(tokens)
+    if lists is not None:
+        ids, off = W.pack_allowed(lists)
+        out = R.token_logprobs(xd, t, top_n, to_dev(ids) if ids.size else
+                               torch.zeros(1, dtype=torch.int32, device="cuda"), off)
+    else:
+        out = R.token_logprobs(xd, t, top_n)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    o = O.token_logprobs(x, tokens, top_n, lists)
+    compare_logprobs(g, o, f"random logprobs {seed}")
