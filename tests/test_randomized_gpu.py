@@ -142,3 +142,34 @@ def test_random_logprob_configuration(seed):
     g = {k: v.cpu().numpy() for k, v in out.items()}
     o = O.token_logprobs(x, tokens, top_n, lists)
     compare_logprobs(g, o, f"random logprobs {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_verify_windows(seed):
+    """Verify windows on seeded random inputs: random window sizes and
+    penalties, drafts that match a random number of leading rows; the
+    accepted counts equal the oracle's for its own tokens."""
+    rng = np.random.default_rng(11000 + seed)
+    window = int(rng.choice([1, 2, 3, 5, 8]))
+    B = window * int(rng.integers(1, 70 // window + 1))
+    V = int(rng.choice([1000, 30011, 120000]))
+    x, kind = _logits(rng, B, V)
+    hist = rng.integers(-2, V + 2, (1, 100)).astype(np.int32)
+    params = _params(rng, B, 1, V)
+    o = O.sample_tokens(x, params, hist, [100])
+    drafts = np.array(o["token"], np.int32)
+    for w in range(B // window):
+        keep = int(rng.integers(0, window + 1))
+        for j in range(keep, window):
+            drafts[w * window + j] = (drafts[w * window + j] + 1) % V
+    say("case random windows", seed, dict(B=B, V=V, window=window, kind=kind))
+    out = R.sample_tokens(to_dev(x), params, to_dev(hist), [100], window=window,
+                          draft=to_dev(drafts))
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    compare_sample(g, o, f"random windows {seed}")
+    exp = O.accept_windows(o["token"], window, drafts)
+    for w in range(B // window):
+        rows = slice(w * window, (w + 1) * window)
+        if np.array_equal(g["token"][rows], o["token"][rows]):
+            assert g["accepted"][w] == exp[w], (seed, w)
