@@ -508,8 +508,9 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the sampler's rows are independent and this "
-              "build runs on a single MI355X; run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the sampler's rows are independent, so a batch "
+              "shards by rows with no exchange and one GPU's share is the measured unit; run it "
+              "with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
