@@ -197,8 +197,8 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     }
 
     uint64_t *list = a.keys + (int64_t)slot * a.keys_stride;
-    // (the fused variant keeps the full 256-key threshold search: the
-    // grouped one pushes its register peak past 96 and it spills)
+    // (the fused variant takes the two-key threshold search without the
+    // full-search rerun: with the rerun its register peak passes 96)
     chunk_topk<EPT, !LP>(sm.s, v, base, V, k, list + (int64_t)chunk * k, masked);
 
     if (raw_sel && !raw_done) {

@@ -216,7 +216,10 @@ __device__ __forceinline__ bool chunk_compact(SelectSmem &sm, float (&v)[EPT], i
     if (wave == 0) {
         const uint32_t lk[4] = {sm.lane_keys[lane], sm.lane_keys[lane + 64],
                                 sm.lane_keys[lane + 128], sm.lane_keys[lane + 192]};
-        const uint32_t t = COARSE ? selection_threshold(lk, k) : kth_largest_key_256_q<16>(lk, k);
+        // COARSE = false (the fused-logprob variant, at its register limit):
+        // the two-key search alone, without the rerun that would spill; a
+        // sparse chunk it misjudges takes the degenerate path, still exact.
+        const uint32_t t = COARSE ? selection_threshold(lk, k) : kth_largest_group_max<16, 2>(lk, k);
         if (lane == 0) sm.thr = t;
     }
     __syncthreads();
