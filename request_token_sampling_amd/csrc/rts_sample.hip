@@ -219,21 +219,42 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         if (!greedy) x0 = philox4x32_10_x0(ctr, R.seed);
     });
 
-    if ((tid >> 6) == 0) epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
-    if (!LP) return;
+    const int wave = tid >> 6, lane = lane_id();
+    if (!LP) {
+        if (wave == 0) epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
+        return;
+    }
 
-    // ---- raw logprobs of the sampled token and the raw top-K
-    __syncthreads();
-    if (raw_sel) list_topk(sm.s, a.raw_keys + (int64_t)slot * a.raw_stride, a.nchunks, K);
-    if ((tid >> 6) != 0) return;
-    const int lane = lane_id();
-    double L;
-    bool uniform;
-    combine_partials(a.partials + (int64_t)slot * a.partial_stride, a.nchunks, &L, &uniform);
-    if (lane == 0) {
+    // ---- with raw logprobs: wave 0 loads the raw logit of every kept id
+    // (the token is one of them) and runs the cuts and the draw while wave 1
+    // combines the chunk partials; neither waits for the other's loads.
+    float xt = 0.0f;  // wave 0: the sampled token's raw logit
+    if (wave == 0) {
+        const uint64_t kept = lane < k ? sm.s.sel[lane] : 0ull;
+        const float xr = kept ? x[key_index(kept)] : 0.0f;
+        epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
         const int32_t t = (int32_t)sm.s.flag;  // the sampled token, left by the epilogue
+        const uint64_t at = __ballot(kept != 0ull && (int32_t)key_index(kept) == t);
+        xt = at ? lane_f32(xr, __ffsll((unsigned long long)at) - 1) : 0.0f;
+    } else if (wave == 1) {
+        double L1;
+        bool u1;
+        combine_partials(a.partials + (int64_t)slot * a.partial_stride, a.nchunks, &L1, &u1);
+        if (lane == 0) {
+            sm.s.red[0] = (uint64_t)__double_as_longlong(L1);
+            sm.s.red[1] = u1 ? 1ull : 0ull;
+        }
+    }
+    __syncthreads();
+    const double L = __longlong_as_double((long long)sm.s.red[0]);
+    const bool uniform = sm.s.red[1] != 0ull;
+    __syncthreads();  // the raw merge below may reuse sm.red
+    if (raw_sel) list_topk(sm.s, a.raw_keys + (int64_t)slot * a.raw_stride, a.nchunks, K);
+    if (wave != 0) return;
+    if (lane == 0) {
+        const int32_t t = (int32_t)sm.s.flag;
         float lp = -INFINITY;
-        if (t >= 0 && t < V) lp = uniform ? (float)(-L) : (float)((double)sanitize(x[t]) - L);
+        if (t >= 0 && t < V) lp = uniform ? (float)(-L) : (float)((double)sanitize(xt) - L);
         a.lp_token[slot] = lp;
     }
     if (lane < K) {
