@@ -537,9 +537,12 @@ template <int EPT, typename ValidCount>
 __device__ __forceinline__ float2 lane_max_sum(const float (&v)[EPT], ValidCount valid_count)
 {
     constexpr float kFltMax = 3.40282346638528859812e+38f;
+    // fmaxf skips NaN, so one operation per element; +inf is clamped once
+    // (m starts at -inf, so it is never NaN).
     float m = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) m = (v[e] == v[e]) ? fmaxf(m, fminf(v[e], kFltMax)) : m;
+    for (int e = 0; e < EPT; ++e) m = fmaxf(m, v[e]);
+    m = fminf(m, kFltMax);
     float s = 0.0f;
     if (m == -INFINITY) {
         s = (float)valid_count();
