@@ -108,12 +108,13 @@ class Workload:
         else:
             w = W.logprobs_stress()
             x = w["logits"]
-            passes = [("sampled+logprobs", w["params"], 40, 40)]
+            passes = [("sampled+logprobs+allowed", w["params"], 40, 40)]
             ids, off = W.pack_allowed(w["allowed"])
             lp = (w["top_n"], ids, off)
             self.desc = ("logprobs stress: 40 bf16-grid rows, V=248,320, top_k 64, min_p 0.1; "
-                         "top-20 raw logprobs of the sampled tokens in the sampling pass, then "
-                         "renormalised over 1,000 allowed ids per row")
+                         "top-20 raw logprobs of the sampled tokens, and the same renormalised "
+                         "over 1,000 allowed ids per row, all in the sampling launch; the "
+                         "two-launch form (renormalisation in a second launch) is timed beside")
         self.B, self.V = x.shape
         self.row_bytes = self.V * 4
         batch_bytes = self.B * self.row_bytes
@@ -126,6 +127,9 @@ class Workload:
         self.ws = R.make_workspace(max([self.B] + [len(p[1]) for p in passes]), self.V, dev)
         self.calls, self.labels = [], []
         self.sampled_rows = 0
+        lp_ids = None if lp is None else torch.from_numpy(lp[1]).to(dev)
+        if lp is not None:
+            spec = dict(spec, logprob_allowed=lp_ids, logprob_allowed_off=lp[2])
         for label, params, counted, stride in passes:
             ctr = torch.tensor([p.get("counter", 0) for p in params], dtype=torch.int64,
                                device=dev)
@@ -138,14 +142,23 @@ class Workload:
         self.param_rows = sum(c.B for c in self.calls)
         self.alt_calls = [R.SampleCall(self.copies[0], params, self.hist, hist_len,
                                        workspace=self.ws) for _, params in self.alt_passes]
-        self.lp_calls = []
+        self.alt_labels = [l for l, _ in self.alt_passes]
+        # bytes a step moves besides the logit rows and the sampling outputs:
+        # logprob outputs, and the allowed lists with the logits they gather
+        self.extra_bytes = 0
         if lp is not None:
             top_n, ids, off = lp
-            tok = self.calls[0].token
-            self.lp_calls = [R.LogprobCall(self.copies[0], tok, top_n,
-                                           torch.from_numpy(ids).to(dev), off,
-                                           workspace=self.ws)]
-        self.passes = [l for l in self.labels] + (["logprobs_allowed"] if self.lp_calls else [])
+            self.extra_bytes = 2 * self.param_rows * (4 + 8 * top_n) + 8 * int(ids.size)
+            # the two-launch form: sampling with raw logprobs, then the
+            # allowed-id logprob kernels on the sampled tokens
+            ctr = torch.tensor([p.get("counter", 0) for p in passes[0][1]], dtype=torch.int64,
+                               device=dev)
+            first = R.SampleCall(self.copies[0], passes[0][1], workspace=self.ws, counters=ctr,
+                                 counter_stride=passes[0][3], logprobs=top_n)
+            self.alt_calls = [first, R.LogprobCall(self.copies[0], first.token, top_n, lp_ids,
+                                                   off, workspace=self.ws)]
+            self.alt_labels = ["sampled+logprobs", "logprobs_allowed"]
+        self.passes = list(self.labels)
         self.torch = torch
 
     @staticmethod
@@ -158,9 +171,6 @@ class Workload:
         x = self.copies[i % self.ncopies]
         for c in self.calls:
             c.logits = self.view(x, c.B)
-            c()
-        for c in self.lp_calls:
-            c.logits = x
             c()
 
 
@@ -226,7 +236,7 @@ def roofline(wl, kern_ms):
     """HBM roofline of the sampler kernel: algorithmic bytes per launch (one
     read of every logit row, plus outputs) over its average launch duration
     (all sampler launches of a step: they are one kernel)."""
-    out_bytes = wl.param_rows * (4 + 12 + 256 + 256 + 4 + 8)
+    out_bytes = wl.param_rows * (4 + 12 + 256 + 256 + 4 + 8) + wl.extra_bytes
     alg = wl.B * wl.row_bytes + out_bytes
     avg_ms = sum(kern_ms) / len(kern_ms)
     achieved = alg / (avg_ms * 1e-3) / 1e9
@@ -316,7 +326,8 @@ def ablations(dev):
 
 def time_alt_graph(wl, steps):
     """Per-step wall time with the passes of a step as separate launches
-    (single stream: the sampled pass, then the greedy pass), graph-replayed."""
+    (single stream: the sampled pass, then the greedy pass; stress: sampling
+    with raw logprobs, then the allowed-id logprob pass), graph-replayed."""
     torch = wl.torch
     for c in wl.alt_calls:
         c()
@@ -368,8 +379,8 @@ def read_traffic(workload):
 
 # The sources rts::sample_kernel is compiled from: the counters in profiles/
 # describe that kernel, so only a change to these makes them stale.
-SAMPLE_KERNEL_SOURCES = ("rts_sample.hip", "rts_epilogue.h", "rts_select.h", "rts_device.h",
-                         "rts_internal.h")
+SAMPLE_KERNEL_SOURCES = ("rts_sample.hip", "rts_epilogue.h", "rts_renorm.h", "rts_select.h",
+                         "rts_device.h", "rts_internal.h")
 
 
 def kernel_source_hash():
@@ -554,7 +565,7 @@ def main():
     if m["alt"] is not None:
         line["separate_launches"] = {"value": round(wl.sampled_rows / m["alt"], 1),
                                      "ms_per_step": round(m["alt"] * 1e3, 5),
-                                     "passes": [l for l, _ in wl.alt_passes]}
+                                     "passes": wl.alt_labels}
     if not args.no_extra:
         extra = {}
         for name in ("batch", "stress", "window"):
@@ -574,6 +585,9 @@ def main():
                                roofline=dict(roofline(w2, m2["kern_ms"]), read_floor=m2["floor"]),
                                desc=w2.desc,
                                passes_per_step=w2.passes)
+            if m2["alt"] is not None:
+                extra[name]["separate_launches"] = dict(ms_per_step=round(m2["alt"] * 1e3, 5),
+                                                        passes=w2.alt_labels)
             del w2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra

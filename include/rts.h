@@ -82,6 +82,25 @@ typedef struct rts_row_params {
  *   top_ids   device int32 [B][top_n]; top_lp device f32 [B][top_n]: the
  *             row's largest raw logits in (logit desc, index asc) order and
  *             their logprobs.  Both may be NULL when top_n = 0.
+ * Optionally, the same values renormalised over allowed_token_ids (#3200,
+ * "Problem and result": the distribution over exactly the listed ids), as
+ * rts_token_logprobs reports them for these lists and the sampled tokens.
+ * The lists do not restrict sampling (rts_sample_extras.allowed does).
+ *   allowed           device int32 ids, row r owning allowed[allowed_off[r]
+ *                     .. allowed_off[r+1]); NULL for none (then the four
+ *                     fields below must be NULL too).  Repeated ids count
+ *                     once and ids outside [0, V) are ignored; a row with
+ *                     an empty list reports the unrestricted values.
+ *   allowed_off       host int64 [B+1], non-decreasing, allowed_off[0] >= 0.
+ *   allowed_token_lp  device f32 [B]: the sampled token's renormalised
+ *                     logprob, -inf when the token is not listed.
+ *   allowed_top_ids / allowed_top_lp  device [B][top_n]: the top listed
+ *                     ids; NULL allowed when top_n = 0.
+ * When no row also has an rts_sample_extras list and every list holds at
+ * most 2,048 ids, these are computed by extra workgroups of the sampling
+ * launch, overlapped with it.  Otherwise a second launch computes them after
+ * the draw, and the lists then need V <= 2^19 as for rts_token_logprobs
+ * (RTS_EINVAL before anything is enqueued).
  */
 typedef struct rts_logprob_request {
     int32_t top_n;
@@ -89,6 +108,11 @@ typedef struct rts_logprob_request {
     float *token_lp;
     int32_t *top_ids;
     float *top_lp;
+    const int32_t *allowed;
+    const int64_t *allowed_off;
+    float *allowed_token_lp;
+    int32_t *allowed_top_ids;
+    float *allowed_top_lp;
 } rts_logprob_request;
 
 /*
@@ -176,7 +200,8 @@ int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream);
  * row, top_p outside (0, 1], min_p outside [0, 1], penalty_repeat <= 0 or
  * non-finite penalties, history_row >= H or set without history, a window
  * longer than RTS_MAX_WINDOW, reserved != 0, an lp request with top_n
- * outside 0..20, reserved != 0 or a NULL output it needs, extras with a
+ * outside 0..20, reserved != 0, a NULL output it needs, bad allowed offsets,
+ * allowed_* fields without allowed, or lists that need V <= 2^19, extras with a
  * window outside 0..64 or not dividing B, missing draft / accepted, or bad
  * allowed offsets, or history offsets (history_row * ldh + length) of 2^31
  * or more; RTS_ENOSPC for a short

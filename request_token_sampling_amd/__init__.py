@@ -54,17 +54,23 @@ assert ctypes.sizeof(RowParams) == 56
 
 class LogprobRequest(ctypes.Structure):
     """Mirror of rts_logprob_request: raw-logit logprobs of the sampled tokens
-    computed in the sampling call's own pass over the logits."""
+    computed in the sampling call's own pass over the logits, optionally also
+    renormalised over per-row allowed lists."""
     _fields_ = [
         ("top_n", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("token_lp", ctypes.c_void_p),
         ("top_ids", ctypes.c_void_p),
         ("top_lp", ctypes.c_void_p),
+        ("allowed", ctypes.c_void_p),
+        ("allowed_off", ctypes.c_void_p),
+        ("allowed_token_lp", ctypes.c_void_p),
+        ("allowed_top_ids", ctypes.c_void_p),
+        ("allowed_top_lp", ctypes.c_void_p),
     ]
 
 
-assert ctypes.sizeof(LogprobRequest) == 32
+assert ctypes.sizeof(LogprobRequest) == 72
 
 
 class SampleExtras(ctypes.Structure):
@@ -174,7 +180,8 @@ class SampleCall:
 
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
                  stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
-                 draft=None, allowed=None, allowed_off=None, ignored=None):
+                 draft=None, allowed=None, allowed_off=None, ignored=None,
+                 logprob_allowed=None, logprob_allowed_off=None):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
@@ -198,6 +205,7 @@ class SampleCall:
         self.counter_stride = int(counter_stride)
         # logprobs=top_n (0..20): raw-logit logprobs of the sampled tokens in the same pass
         self.lp = None
+        self.lp_allowed = None
         if logprobs is not None:
             n = int(logprobs)
             self.token_lp = torch.empty(self.B, dtype=torch.float32, device=dev)
@@ -206,6 +214,22 @@ class SampleCall:
             self.lp = LogprobRequest(n, 0, self.token_lp.data_ptr(),
                                      self.top_ids.data_ptr() if n > 0 else None,
                                      self.top_lp.data_ptr() if n > 0 else None)
+            # the same, renormalised over per-row allowed lists (not a mask)
+            self.lp_allowed = logprob_allowed
+            if logprob_allowed is not None:
+                if logprob_allowed.dtype != torch.int32 or not logprob_allowed.is_cuda:
+                    raise ValueError("logprob_allowed must be a CUDA int32 tensor")
+                self.lp_allowed_off = np.ascontiguousarray(logprob_allowed_off, dtype=np.int64)
+                self.a_token_lp = torch.empty(self.B, dtype=torch.float32, device=dev)
+                self.a_top_ids = torch.empty((self.B, max(n, 0)), dtype=torch.int32, device=dev)
+                self.a_top_lp = torch.empty((self.B, max(n, 0)), dtype=torch.float32, device=dev)
+                self.lp.allowed = logprob_allowed.data_ptr()
+                self.lp.allowed_off = self.lp_allowed_off.ctypes.data_as(ctypes.c_void_p)
+                self.lp.allowed_token_lp = self.a_token_lp.data_ptr()
+                self.lp.allowed_top_ids = self.a_top_ids.data_ptr() if n > 0 else None
+                self.lp.allowed_top_lp = self.a_top_lp.data_ptr() if n > 0 else None
+        elif logprob_allowed is not None:
+            raise ValueError("logprob_allowed needs logprobs=top_n")
         # verify windows (window rows each, drafts per row) and allowed-id masks
         self.ex = None
         self.accepted = None
@@ -261,6 +285,9 @@ class SampleCall:
                  kept_logits=self.kept_logits, philox_x0=self.philox_x0)
         if self.lp is not None:
             r.update(token_lp=self.token_lp, top_ids=self.top_ids, top_lp=self.top_lp)
+            if self.lp_allowed is not None:
+                r.update(allowed_token_lp=self.a_token_lp, allowed_top_ids=self.a_top_ids,
+                         allowed_top_lp=self.a_top_lp)
         if self.accepted is not None:
             r.update(accepted=self.accepted)
         return r
@@ -268,7 +295,8 @@ class SampleCall:
 
 def sample_tokens(logits, params, history=None, history_len=None, workspace=None,
                   stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
-                  draft=None, allowed=None, allowed_off=None, ignored=None) -> dict:
+                  draft=None, allowed=None, allowed_off=None, ignored=None,
+                  logprob_allowed=None, logprob_allowed_off=None) -> dict:
     """Run the sampling chain over the rows of `logits` (CUDA float32 [B][V]).
 
     params: list of per-row dicts (keys of rts_row_params; missing keys neutral).
@@ -284,10 +312,15 @@ def sample_tokens(logits, params, history=None, history_len=None, workspace=None
     allowed, allowed_off: CUDA int32 ids with host int64 offsets [B+1]; a row
     with a non-empty list samples only among those ids.
     ignored: optional CUDA int32 [1] counter; the call adds the number of
-    device ids it read and ignored (outside [0, V))."""
+    device ids it read and ignored (outside [0, V)).
+    logprob_allowed, logprob_allowed_off (with logprobs): CUDA int32 ids with
+    host int64 offsets [B+1]; adds allowed_token_lp[B], allowed_top_ids and
+    allowed_top_lp[B][top_n], the logprobs renormalised over each row's list
+    (an empty list: the unrestricted values).  The lists do not restrict
+    sampling."""
     return SampleCall(logits, params, history, history_len, workspace, stream, counters,
                       counter_stride, logprobs, window, draft, allowed, allowed_off,
-                      ignored)().results()
+                      ignored, logprob_allowed, logprob_allowed_off)().results()
 
 
 class LogprobCall:

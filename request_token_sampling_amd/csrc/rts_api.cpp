@@ -149,6 +149,106 @@ void pack_row(rts::SampleRow &s, const rts_row_params &p, int64_t V, const int32
     s.pack = (uint32_t)n_eff | ((uint32_t)k_eff << 16) | (greedy ? (1u << 24) : 0u);
 }
 
+// Per-row offsets into an id list: off[0] >= 0 and never decreasing.
+int check_offsets(int64_t B, const int64_t *off, const char *what)
+{
+    if (off[0] < 0) return fail(RTS_EINVAL, "%s[0] < 0", what);
+    for (int64_t r = 0; r < B; ++r)
+        if (off[r + 1] < off[r]) return fail(RTS_EINVAL, "%s decreases at row %lld", what, (long long)r);
+    return RTS_OK;
+}
+
+// The allowed-id logprob kernels keep a vocabulary bitmap in LDS: sets
+// *fast_fits when the gather-once kernel's LDS fits too.
+int check_allowed_lds(int64_t V, bool *fast_fits)
+{
+    const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
+    const size_t max_lds = V > (1 << 19) ? 0 : max_lds_per_block();
+    if (bitmap_bytes + rts::kAllowedStaticLds > max_lds)
+        return fail(RTS_EINVAL, "allowed lists need V <= 2^19 (V = %lld)", (long long)V);
+    *fast_fits = bitmap_bytes + rts::kAllowedStaticLds <= max_lds;
+    return RTS_OK;
+}
+
+// The launches of rts_token_logprobs once its arguments are checked.  Rows
+// with an empty list take the full-row reducer, unless `restricted_only`
+// leaves them out; short lists take the gather-once kernel, longer ones the
+// bitmap-walking kernel.  ld = 0 makes every row read row 0.
+int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, const int32_t *tokens,
+                     int32_t top_n, const int32_t *allowed, const int64_t *allowed_off,
+                     float *token_lp, int32_t *top_ids, float *top_lp, void *workspace,
+                     bool restricted_only, bool fast_fits, hipStream_t stream)
+{
+    const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
+    bool any_restricted = false;
+    if (allowed != nullptr)
+        for (int64_t r = 0; r < B && !any_restricted; ++r)
+            any_restricted = allowed_off[r + 1] > allowed_off[r];
+
+    char *ws = static_cast<char *>(workspace);
+    rts::LogprobArgs base;
+    std::memset(&base, 0, sizeof base);
+    base.logits = logits;
+    base.ld = ld;
+    base.tokens = tokens;
+    base.allowed = allowed;
+    const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
+    const rts::WsLayout L = rts::ws_layout(rows_ws, V);
+    base.keys = reinterpret_cast<uint64_t *>(ws + L.keys);
+    base.tickets = reinterpret_cast<uint32_t *>(ws + rts::kTicketRegion);
+    base.token_lp = token_lp;
+    base.top_ids = top_ids;
+    base.top_lp = top_lp;
+    base.V = (int32_t)V;
+    base.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
+    base.partial_stride = (int32_t)rts::max_chunks(V);
+    base.top_n = top_n;
+    base.partials = reinterpret_cast<float2 *>(ws + L.partials);
+
+    // kind 0: unrestricted rows (full-row reducer); 1: short lists; 2: long lists.
+    // Each kind in launches of up to 64 rows.
+    for (int kind = restricted_only ? 1 : 0; kind < 3; ++kind) {
+        if (kind > 0 && !any_restricted) break;
+        rts::LogprobArgs a = base;
+        int n = 0;
+        auto flush = [&]() -> int {
+            if (n == 0) return 0;
+            a.rows = n;
+            int e;
+            if (kind == 0) {
+                const bool vec = is_vec_ok(logits, ld);
+                int ept = choose_ept(n, V);
+                if (!vec && ept > 16) ept = 16;  // as for sampling: the scalar-load form spills at 32
+                a.nchunks = (int32_t)chunks_for(V, ept);
+                a.early_xcds = n * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
+                e = rts::launch_logprobs_full(a, ept, vec, stream);
+            } else {
+                e = rts::launch_logprobs_allowed(a, bitmap_bytes, kind == 2, stream);
+            }
+            n = 0;
+            return e;
+        };
+        for (int64_t r = 0; r < B; ++r) {
+            const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
+            const int row_kind = cnt == 0 ? 0 : ((fast_fits && cnt <= rts::kAllowedFast) ? 1 : 2);
+            if (row_kind != kind) continue;
+            rts::LogprobRow &lr = a.row[n++];
+            lr.row = (int32_t)r;
+            lr.allowed_off = allowed ? allowed_off[r] : 0;
+            lr.allowed_cnt = cnt;
+            lr.pad = 0;
+            if (n == rts::kRowsPerLaunch) {
+                const int e = flush();
+                if (e != 0)
+                    return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
+            }
+        }
+        const int e = flush();
+        if (e != 0) return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
+    }
+    return RTS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +319,18 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         if (lp->token_lp == nullptr) return fail(RTS_EINVAL, "lp->token_lp is NULL");
         if (lp->top_n > 0 && (lp->top_ids == nullptr || lp->top_lp == nullptr))
             return fail(RTS_EINVAL, "lp->top_ids / lp->top_lp are NULL with top_n = %d", lp->top_n);
+        if (lp->allowed != nullptr) {
+            if (lp->allowed_off == nullptr) return fail(RTS_EINVAL, "lp->allowed without allowed_off");
+            if (lp->allowed_token_lp == nullptr)
+                return fail(RTS_EINVAL, "lp->allowed_token_lp is NULL with lp->allowed");
+            if (lp->top_n > 0 && (lp->allowed_top_ids == nullptr || lp->allowed_top_lp == nullptr))
+                return fail(RTS_EINVAL, "lp->allowed_top_ids / allowed_top_lp are NULL with top_n = %d",
+                            lp->top_n);
+            if (const int e = check_offsets(B, lp->allowed_off, "lp->allowed_off")) return e;
+        } else if (lp->allowed_off != nullptr || lp->allowed_token_lp != nullptr ||
+                   lp->allowed_top_ids != nullptr || lp->allowed_top_lp != nullptr) {
+            return fail(RTS_EINVAL, "lp->allowed_* outputs or offsets without lp->allowed");
+        }
     }
     const int window = ex ? ex->window : 0;
     const int32_t *allowed = ex ? ex->allowed : nullptr;
@@ -234,10 +346,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             return fail(RTS_EINVAL, "ex->draft / ex->accepted are NULL with window = %d", window);
         if (allowed != nullptr) {
             if (allowed_off == nullptr) return fail(RTS_EINVAL, "ex->allowed without allowed_off");
-            if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");
-            for (int64_t r = 0; r < B; ++r)
-                if (allowed_off[r + 1] < allowed_off[r])
-                    return fail(RTS_EINVAL, "allowed_off decreases at row %lld", (long long)r);
+            if (const int e = check_offsets(B, allowed_off, "allowed_off")) return e;
             if (allowed_off[B] > 0x7FFFFFFFLL)
                 return fail(RTS_EINVAL, "allowed_off[B] = %lld >= 2^31", (long long)allowed_off[B]);
         }
@@ -246,6 +355,21 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     rts_workspace_bytes(B, V, &need);
     if (ws_bytes < need)
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
+
+    // Logprobs renormalised over allowed lists: in the sampling launch itself
+    // when no row also has a candidate list and every list is short enough;
+    // else by the allowed-id logprob kernels after it, on the sampled tokens.
+    const int32_t *lpa = lp ? lp->allowed : nullptr;
+    const int64_t *lpa_off = lpa ? lp->allowed_off : nullptr;
+    int64_t lpa_max = 0;
+    bool lpa_fused = false, lpa_fast = false;
+    if (lpa != nullptr) {
+        for (int64_t r = 0; r < B; ++r)
+            if (lpa_off[r + 1] - lpa_off[r] > lpa_max) lpa_max = lpa_off[r + 1] - lpa_off[r];
+        lpa_fused = allowed == nullptr && lpa_max <= rts::kRenormMax && lpa_off[B] <= 0x7FFFFFFFLL;
+        if (!lpa_fused && lpa_max > 0)
+            if (const int e = check_allowed_lds(V, &lpa_fast)) return e;
+    }
 
     // Check every row before enqueuing anything.
     if (const int e = check_rows(B, params, history, H, ldh, history_len)) return e;
@@ -301,15 +425,39 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             a.lp_ids = lp->top_n > 0 ? lp->top_ids + r0 * lp->top_n : nullptr;
             a.lp_top = lp->top_n > 0 ? lp->top_lp + r0 * lp->top_n : nullptr;
         }
-        for (int i = 0; i < rows; ++i)
-            pack_row(a.row[i], params[r0 + i], V, history_len, ldh,
-                     allowed ? (int32_t)allowed_off[r0 + i] : 0,
-                     allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0);
+        if (lpa != nullptr) {
+            // rows without a list get the unrestricted values here; with the
+            // allowed-id kernels, listed rows are overwritten after the launch
+            a.lpa_token = lp->allowed_token_lp + r0;
+            a.lpa_ids = lp->top_n > 0 ? lp->allowed_top_ids + r0 * lp->top_n : nullptr;
+            a.lpa_top = lp->top_n > 0 ? lp->allowed_top_lp + r0 * lp->top_n : nullptr;
+            a.lpa_w = reinterpret_cast<uint64_t *>(ws + rts::kTicketRegion);
+            if (lpa_fused && lpa_max > 0) {
+                a.allowed = lpa;
+                a.lpa_blocks = rows;  // after the sampling grid, one per row
+            }
+        }
+        for (int i = 0; i < rows; ++i) {
+            if (a.lpa_blocks > 0) {
+                const int64_t c = lpa_off[r0 + i + 1] - lpa_off[r0 + i];
+                pack_row(a.row[i], params[r0 + i], V, history_len, ldh, (int32_t)lpa_off[r0 + i],
+                         (int32_t)c);
+                if (c > 0) a.row[i].pack |= rts::kPackRenorm;
+            } else {
+                pack_row(a.row[i], params[r0 + i], V, history_len, ldh,
+                         allowed ? (int32_t)allowed_off[r0 + i] : 0,
+                         allowed ? (int32_t)(allowed_off[r0 + i + 1] - allowed_off[r0 + i]) : 0);
+            }
+        }
         const int e = rts::launch_sample(a, ept, vec, stream);
         if (e != 0)
             return fail(RTS_EDEVICE, "sample launch (rows %lld..%lld): %s", (long long)r0,
                         (long long)(r0 + rows - 1), hipGetErrorString((hipError_t)e));
     }
+    if (lpa != nullptr && !lpa_fused && lpa_max > 0)
+        return enqueue_logprobs(logits, B, V, ld, token, lp->top_n, lpa, lpa_off,
+                                lp->allowed_token_lp, lp->allowed_top_ids, lp->allowed_top_lp,
+                                workspace, true, lpa_fast, stream);
     return RTS_OK;
 }
 
@@ -342,87 +490,16 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     // Restricted rows take the gather-once kernel when their list is short
     // enough, else the bitmap-walking kernel; both keep a vocabulary bitmap
     // in LDS.
-    const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
-    const size_t fast_lds = bitmap_bytes;
     bool any_restricted = false, fast_fits = false;
     if (allowed != nullptr) {
-        if (allowed_off[0] < 0) return fail(RTS_EINVAL, "allowed_off[0] < 0");
-        for (int64_t r = 0; r < B; ++r) {
-            if (allowed_off[r + 1] < allowed_off[r])
-                return fail(RTS_EINVAL, "allowed_off decreases at row %lld", (long long)r);
+        if (const int e = check_offsets(B, allowed_off, "allowed_off")) return e;
+        for (int64_t r = 0; r < B; ++r)
             if (allowed_off[r + 1] > allowed_off[r]) any_restricted = true;
-        }
-        if (any_restricted) {
-            const size_t max_lds = V > (1 << 19) ? 0 : max_lds_per_block();
-            if (bitmap_bytes + rts::kAllowedStaticLds > max_lds)
-                return fail(RTS_EINVAL, "allowed lists need V <= 2^19 (V = %lld)", (long long)V);
-            fast_fits = fast_lds + rts::kAllowedStaticLds <= max_lds;
-        }
+        if (any_restricted)
+            if (const int e = check_allowed_lds(V, &fast_fits)) return e;
     }
-
-    char *ws = static_cast<char *>(workspace);
-    rts::LogprobArgs base;
-    std::memset(&base, 0, sizeof base);
-    base.logits = logits;
-    base.ld = ld;
-    base.tokens = tokens;
-    base.allowed = allowed;
-    const int64_t rows_ws = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
-    const rts::WsLayout L = rts::ws_layout(rows_ws, V);
-    base.keys = reinterpret_cast<uint64_t *>(ws + L.keys);
-    base.tickets = reinterpret_cast<uint32_t *>(ws + rts::kTicketRegion);
-    base.token_lp = token_lp;
-    base.top_ids = top_ids;
-    base.top_lp = top_lp;
-    base.V = (int32_t)V;
-    base.keys_stride = (int32_t)(rts::keys_bytes_per_row(V) / 8u);
-    base.partial_stride = (int32_t)rts::max_chunks(V);
-    base.top_n = top_n;
-    base.partials = reinterpret_cast<float2 *>(ws + L.partials);
-
-    // kind 0: unrestricted rows (full-row reducer); 1: short lists; 2: long lists.
-    // Each kind in launches of up to 64 rows.
-    for (int kind = 0; kind < 3; ++kind) {
-        if (kind > 0 && !any_restricted) break;
-        rts::LogprobArgs a = base;
-        int n = 0;
-        auto flush = [&]() -> int {
-            if (n == 0) return 0;
-            a.rows = n;
-            int e;
-            if (kind == 0) {
-                const bool vec = is_vec_ok(logits, ld);
-                int ept = choose_ept(n, V);
-                if (!vec && ept > 16) ept = 16;  // as for sampling: the scalar-load form spills at 32
-                a.nchunks = (int32_t)chunks_for(V, ept);
-                a.early_xcds = n * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
-                e = rts::launch_logprobs_full(a, ept, vec, stream);
-            } else {
-                e = rts::launch_logprobs_allowed(a, kind == 1 ? fast_lds : bitmap_bytes,
-                                                 kind == 2, stream);
-            }
-            n = 0;
-            return e;
-        };
-        for (int64_t r = 0; r < B; ++r) {
-            const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
-            const int row_kind = cnt == 0 ? 0 : ((fast_fits && cnt <= rts::kAllowedFast) ? 1 : 2);
-            if (row_kind != kind) continue;
-            rts::LogprobRow &lr = a.row[n++];
-            lr.row = (int32_t)r;
-            lr.allowed_off = allowed ? allowed_off[r] : 0;
-            lr.allowed_cnt = cnt;
-            lr.pad = 0;
-            if (n == rts::kRowsPerLaunch) {
-                const int e = flush();
-                if (e != 0)
-                    return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
-            }
-        }
-        const int e = flush();
-        if (e != 0) return fail(RTS_EDEVICE, "logprob launch: %s", hipGetErrorString((hipError_t)e));
-    }
-    return RTS_OK;
+    return enqueue_logprobs(logits, B, V, ld, tokens, top_n, allowed, allowed_off, token_lp, top_ids,
+                            top_lp, workspace, false, fast_fits, stream);
 }
 
 int rts_sample_tokens_prior(int design, const float *logits, int64_t B, int64_t V, int64_t ld,

@@ -37,6 +37,16 @@ constexpr size_t kAllowedStaticLds = 10240;
 // bitmap in every pass.
 constexpr int kAllowedPerThread = 16;
 constexpr int kAllowedFast = kAllowedPerThread * kBlock;
+// A sampling call that also renormalises its logprobs over allowed lists does
+// it in the same launch when every list holds at most kRenormMax ids: one
+// extra workgroup per row gathers the list (kRenormPerThread ids a thread)
+// and drops repeats with a kRenormSlots-entry hash table in LDS.
+constexpr int kRenormPerThread = 8;
+constexpr int kRenormMax = kRenormPerThread * kBlock;
+constexpr int kRenormSlots = 2 * kRenormMax;
+// SampleRow.pack bit: the row's allowed list renormalises its logprobs and
+// does not restrict its candidates.
+constexpr uint32_t kPackRenorm = 1u << 25;
 
 inline int64_t max_chunks(int64_t V) { return (V + kMinChunk - 1) / kMinChunk; }
 inline size_t keys_bytes_per_row(int64_t V) { return (size_t)max_chunks(V) * kMaxK * 8u; }
@@ -70,7 +80,7 @@ struct SampleRow {
     float rep;
     float freq;
     float present;
-    uint32_t pack;         // bits 0..15 window length, 16..22 k_eff, 24 greedy
+    uint32_t pack;         // bits 0..15 window length, 16..22 k_eff, 24 greedy, 25 kPackRenorm
     int32_t allowed_cnt;   // 0: every id is a candidate
 };
 static_assert(sizeof(SampleRow) == 56, "argument block layout");
@@ -97,7 +107,7 @@ struct SampleArgs {
     int32_t lp_on;         // 1: compute the raw logprobs of the sampled token
     int32_t raw_stride;    // raw top-K keys per row slot in the workspace
     int32_t partial_stride;
-    int32_t pad2_;
+    int32_t lpa_blocks;    // trailing workgroups that renormalise over allowed lists (0: none)
     uint64_t *raw_keys;    // workspace: per row slot nchunks * lp_topn keys
     uint64_t *partials;    // workspace: per row slot nchunks (max, sum) pairs
     float *lp_token;       // outputs, row 0 of this launch
@@ -110,6 +120,10 @@ struct SampleArgs {
     uint32_t *ignored;       // device count of ids read and ignored (outside [0, V)), or NULL
     int32_t window;          // rows per verify window; 0: none
     int32_t chunk_major;     // 1: rows share one logits row; a chunk's rows share an XCD
+    float *lpa_token;        // logprobs over allowed lists (NULL: not asked), row 0 of this launch
+    int32_t *lpa_ids;
+    float *lpa_top;
+    uint64_t *lpa_w;         // workspace: one rendezvous word per row slot, 128 bytes apart
     SampleRow row[kRowsPerLaunch];
 };
 // HIP passes at most 4 KiB of kernel arguments.
@@ -149,7 +163,10 @@ struct LogprobArgs {
 constexpr int kEarlyXcdWork = 64;
 
 // Grid for `work` workgroups, padded for early-XCD placement when it applies.
-inline unsigned grid_for(int work, int early) { return early ? (unsigned)(((work + 1) / 2) * 8) : (unsigned)work; }
+__host__ __device__ inline unsigned grid_for(int work, int early)
+{
+    return early ? (unsigned)(((work + 1) / 2) * 8) : (unsigned)work;
+}
 
 // XCDs a launch's work is spread over (logical_block): 2 for early-XCD launches.
 __host__ __device__ inline int xcds_used(int early) { return early ? 2 : 8; }

@@ -17,6 +17,7 @@
 // captured graph replaying the call keeps drawing fresh numbers ("Problem":
 // a captured sampler would otherwise repeat its draws).
 #include "rts_epilogue.h"
+#include "rts_renorm.h"
 
 namespace rts {
 
@@ -24,9 +25,11 @@ template <int EPT, bool LP>
 struct SampleSmem {
     SelectSmem s;
     uint32_t pen_bits[EPT * kBlock / 32];  // one bit per id of the chunk
-    uint32_t pen_cnt[EPT * kBlock / 2];    // two 16-bit counts per word
+    // two 16-bit counts per word; a renormalising workgroup's hash table
+    uint32_t pen_cnt[(LP && EPT * kBlock / 2 < kRenormSlots) ? kRenormSlots : EPT * kBlock / 2];
     uint64_t raw_keys[LP ? 4 * kRegion : 1];  // candidates of the raw top-K
     uint32_t raw_cnt[4];
+    uint32_t lpa_member[2];  // the sampled token is in the row's allowed list (waves 2, 3)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +68,15 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     constexpr int NQ = EPT / 4;
     __shared__ SampleSmem<EPT, LP> sm;
 
+    if constexpr (LP) {
+        // workgroups past the sampling grid renormalise over allowed lists
+        const int nsamp =
+            (int)grid_for(sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major), a.early_xcds);
+        if ((int)blockIdx.x >= nsamp) {
+            renorm_block(a, sm.s, sm.pen_cnt, (int)blockIdx.x - nsamp);
+            return;
+        }
+    }
     const int tid = threadIdx.x;
     const int lb = logical_block(a.early_xcds);
     if (lb < 0 || lb >= sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major)) return;
@@ -102,7 +114,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // ranked after the penalised selection, so only one set of values is
     // held in registers at a time.
     const int K = LP ? a.lp_topn : 0;
-    const bool masked = R.allowed_cnt > 0;
+    // an allowed list restricts the candidates unless it only renormalises
+    // the logprobs
+    const bool masked = R.allowed_cnt > 0 && (R.pack & kPackRenorm) == 0u;
     const bool raw_sel = LP && K > 0 && !(n_eff == 0 && !masked && k >= K);
     const Cands rawc{sm.raw_keys, sm.raw_cnt};
     uint64_t *raw_out = LP ? a.raw_keys + (int64_t)slot * a.raw_stride + (int64_t)chunk * K : nullptr;
@@ -227,13 +241,23 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
 
     // ---- with raw logprobs: wave 0 loads the raw logit of every kept id
     // (the token is one of them) and runs the cuts and the draw while wave 1
-    // combines the chunk partials; neither waits for the other's loads.
-    float xt = 0.0f;  // wave 0: the sampled token's raw logit
+    // combines the chunk partials; neither waits for the other's loads.  On a
+    // row renormalised over an allowed list, waves 2 and 3 load the list
+    // meanwhile, and wave 0 meets the row's renormalising workgroup (see
+    // rts_renorm.h) once the token is published.
+    const bool renorm = (R.pack & kPackRenorm) != 0u;
+    uint64_t *const lpa_w = a.lpa_w + (int64_t)slot * (kTicketStride / 2);
+    float xt = 0.0f;      // wave 0: the sampled token's raw logit
+    uint64_t enc = 0ull;  // wave 0, lane 0: the renormalising workgroup's enc(L), 0 if not done
     if (wave == 0) {
         const uint64_t kept = lane < k ? sm.s.sel[lane] : 0ull;
         const float xr = kept ? x[key_index(kept)] : 0.0f;
+        if (renorm && lane == 0) enc = read_published_u64(lpa_w);  // done already?
         epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
         const int32_t t = (int32_t)sm.s.flag;  // the sampled token, left by the epilogue
+        if (renorm && lane == 0 && enc == 0ull)
+            enc = __hip_atomic_exchange(lpa_w, kSamplerTag | (uint32_t)t, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t at = __ballot(kept != 0ull && (int32_t)key_index(kept) == t);
         xt = at ? lane_f32(xr, __ffsll((unsigned long long)at) - 1) : 0.0f;
     } else if (wave == 1) {
@@ -244,25 +268,51 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
             sm.s.red[0] = (uint64_t)__double_as_longlong(L1);
             sm.s.red[1] = u1 ? 1ull : 0ull;
         }
+    } else if (renorm) {
+        // the list into LDS (the penalty counts' space, free by now)
+        const int32_t *ids = a.allowed + R.allowed_off;
+        for (int f = tid - 128; f < R.allowed_cnt; f += 128)
+            sm.pen_cnt[f] = (uint32_t)ids[f];
     }
     __syncthreads();
     const double L = __longlong_as_double((long long)sm.s.red[0]);
     const bool uniform = sm.s.red[1] != 0ull;
+    if (renorm && wave >= 2) {
+        const int32_t t = (int32_t)sm.s.flag;
+        bool hit = false;
+        for (int f = tid - 128; f < R.allowed_cnt; f += 128) hit = hit || ((int32_t)sm.pen_cnt[f] == t);
+        const uint64_t b = __ballot(hit && t >= 0 && t < V);
+        if (lane == 0) sm.lpa_member[wave - 2] = b ? 1u : 0u;
+    }
     __syncthreads();  // the raw merge below may reuse sm.red
     if (raw_sel) list_topk(sm.s, a.raw_keys + (int64_t)slot * a.raw_stride, a.nchunks, K);
     if (wave != 0) return;
+    const bool lpa_copy = a.lpa_token != nullptr && !renorm;  // unrestricted: the same values
     if (lane == 0) {
         const int32_t t = (int32_t)sm.s.flag;
         float lp = -INFINITY;
         if (t >= 0 && t < V) lp = uniform ? (float)(-L) : (float)((double)sanitize(xt) - L);
         a.lp_token[slot] = lp;
+        if (lpa_copy) a.lpa_token[slot] = lp;
+        if (renorm && enc != 0ull) {
+            // the renormalising workgroup finished first: this one writes
+            const bool member = (sm.lpa_member[0] | sm.lpa_member[1]) != 0u;
+            a.lpa_token[slot] = renorm_token_lp(enc, member, xt);
+            publish_u64(lpa_w, 0ull);
+        }
     }
     if (lane < K) {
         const uint64_t key = sm.s.sel[lane];
         const bool valid = key != 0ull;
-        a.lp_ids[(int64_t)slot * K + lane] = valid ? (int32_t)key_index(key) : -1;
-        a.lp_top[(int64_t)slot * K + lane] =
+        const int32_t tid_out = valid ? (int32_t)key_index(key) : -1;
+        const float lp_out =
             valid ? (uniform ? (float)(-L) : (float)((double)key_logit(key) - L)) : -INFINITY;
+        a.lp_ids[(int64_t)slot * K + lane] = tid_out;
+        a.lp_top[(int64_t)slot * K + lane] = lp_out;
+        if (lpa_copy) {
+            a.lpa_ids[(int64_t)slot * K + lane] = tid_out;
+            a.lpa_top[(int64_t)slot * K + lane] = lp_out;
+        }
     }
 }
 
@@ -271,7 +321,8 @@ static int launch_t(const SampleArgs &a, hipStream_t s)
 {
     hipLaunchKernelGGL((sample_kernel<EPT, VEC, LP>),
                        dim3(grid_for(sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major),
-                                     a.early_xcds)),
+                                     a.early_xcds) +
+                            a.lpa_blocks),
                        dim3(kBlock), 0, s, a);
     return (int)hipGetLastError();
 }

@@ -45,9 +45,10 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(R.RowParams) == 56
     body = text[text.index("typedef struct rts_logprob_request"):
                 text.index("} rts_logprob_request;")]
-    fields = re.findall(r"^\s*(?:float|int32_t)\s*\*?\s*(\w+);", body, flags=re.M)
+    fields = re.findall(r"^\s*(?:const\s+)?(?:float|int32_t|int64_t)\s*\*?\s*(\w+);", body,
+                        flags=re.M)
     assert fields == [f for f, _ in R.LogprobRequest._fields_]
-    assert ctypes.sizeof(R.LogprobRequest) == 32
+    assert ctypes.sizeof(R.LogprobRequest) == 72
     body = text[text.index("typedef struct rts_sample_extras"):text.index("} rts_sample_extras;")]
     fields = re.findall(r"^\s*(?:const\s+)?(?:int32_t|int64_t|uint32_t)\s*\*?\s*(\w+);", body, flags=re.M)
     assert fields == [f for f, _ in R.SampleExtras._fields_]
@@ -148,6 +149,57 @@ def test_logprob_request_without_top_entries_needs_no_top_buffers():
     lp = R.LogprobRequest(top_n=0, reserved=0, token_lp=4096, top_ids=None, top_lp=None)
     assert sample([dict(SAMPLED, top_k=0)], lp=lp) == R.RTS_EINVAL
     assert "top_k" in last_error()
+
+
+def lp_allowed_request(off, **kw):
+    d = dict(top_n=5, reserved=0, token_lp=4096, top_ids=4096, top_lp=4096, allowed=4096,
+             allowed_off=None if off is None else ctypes.cast(off, ctypes.c_void_p),
+             allowed_token_lp=4096, allowed_top_ids=4096, allowed_top_lp=4096)
+    d.update(kw)
+    return R.LogprobRequest(**d)
+
+
+def test_bad_renormalising_logprob_request_is_refused():
+    rows = [dict(SAMPLED) for _ in range(4)]
+    off_ok = (ctypes.c_int64 * 5)(0, 3, 3, 10, 12)
+    off_down = (ctypes.c_int64 * 5)(0, 3, 2, 10, 12)
+    off_neg = (ctypes.c_int64 * 5)(-1, 3, 3, 10, 12)
+    cases = [
+        (lp_allowed_request(None), "allowed_off"),
+        (lp_allowed_request(off_ok, allowed_token_lp=None), "allowed_token_lp"),
+        (lp_allowed_request(off_ok, allowed_top_ids=None), "allowed_top_ids"),
+        (lp_allowed_request(off_ok, allowed_top_lp=None), "allowed_top_lp"),
+        (lp_allowed_request(off_down), "decreases"),
+        (lp_allowed_request(off_neg), "[0]"),
+        (lp_allowed_request(off_ok, allowed=None), "without lp->allowed"),
+    ]
+    for lp, word in cases:
+        assert sample(rows, lp=lp) == R.RTS_EINVAL, word
+        assert word in last_error(), (word, last_error())
+    # top_n = 0 needs no top buffers; the bad row then names itself
+    lp = lp_allowed_request(off_ok, top_n=0, top_ids=None, top_lp=None, allowed_top_ids=None,
+                            allowed_top_lp=None)
+    assert sample(rows[:3] + [dict(SAMPLED, top_k=0)], lp=lp) == R.RTS_EINVAL
+    assert "row 3" in last_error(), last_error()
+
+
+def test_renormalising_lists_beyond_the_fused_path_need_small_vocabularies():
+    """Lists longer than 2,048 ids, or lists on rows that also restrict their
+    candidates, take the allowed-id logprob kernels, whose vocabulary bitmap
+    needs V <= 2^19: refused before anything is enqueued.  Short lists have
+    no such limit (they pass validation and fail on the bad row)."""
+    V = 2 ** 20
+    rows = [dict(SAMPLED), dict(SAMPLED, top_k=0)]
+    long_off = (ctypes.c_int64 * 3)(0, 2049, 2049)
+    short_off = (ctypes.c_int64 * 3)(0, 2048, 2048)
+    assert sample(rows, V=V, lp=lp_allowed_request(long_off)) == R.RTS_EINVAL
+    assert "2^19" in last_error(), last_error()
+    assert sample(rows, V=V, lp=lp_allowed_request(short_off)) == R.RTS_EINVAL
+    assert "row 1" in last_error(), last_error()
+    mask_off = (ctypes.c_int64 * 3)(0, 1, 1)
+    ex = extras(allowed=4096, allowed_off=ctypes.cast(mask_off, ctypes.c_void_p))
+    assert sample(rows, V=V, lp=lp_allowed_request(short_off), ex=ex) == R.RTS_EINVAL
+    assert "2^19" in last_error(), last_error()
 
 
 def extras(**kw):
