@@ -50,6 +50,9 @@ def parse():
                          "reads cold rows (used for the rocprofv3 kernel averages)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads' figures in the JSON line")
+    ap.add_argument("--no-alt", action="store_true",
+                    help="skip the separate-launch comparison, so every launch of the sampler "
+                         "kernel in the run is the step's own (used for the rocprofv3 averages)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (known bytes) for counter scaling")
@@ -348,12 +351,12 @@ def time_alt_graph(wl, steps):
     return wall / steps
 
 
-def measure(wl, steps, warmup, warm=True):
+def measure(wl, steps, warmup, warm=True, alt=True):
     eager = time_eager(wl, steps, warmup)
     graph = time_graph(wl, steps)
     warm = time_graph(wl, steps, warm=True) if warm else None
     kern = kernel_durations(wl, min(steps, 500))
-    alt = time_alt_graph(wl, steps) if wl.alt_calls else None
+    alt = time_alt_graph(wl, steps) if (alt and wl.alt_calls) else None
     return dict(graph_wall=graph, warm_wall=warm, eager_wall=eager, kern_ms=kern,
                 floor=read_floor(wl), alt=alt)
 
@@ -532,7 +535,7 @@ def main():
         calibration_copy(dev)
     wl = Workload(args.workload, dev)
     progress(f"{args.workload}: {wl.ncopies} copies resident, timing {args.steps} steps")
-    m = measure(wl, args.steps, args.warmup, warm=not args.no_warm)
+    m = measure(wl, args.steps, args.warmup, warm=not args.no_warm, alt=not args.no_alt)
     progress(f"{args.workload}: graph {m['graph_wall'] / args.steps * 1e3:.4f} ms/step, eager "
              f"{m['eager_wall'] / args.steps * 1e3:.4f} ms/step, kernels {m['kern_ms']}")
     value = wl.sampled_rows * args.steps / m["graph_wall"]
@@ -573,7 +576,8 @@ def main():
                 continue
             w2 = Workload(name, dev)
             steps = max(50, args.steps // 4)
-            m2 = measure(w2, steps, max(10, args.warmup // 4), warm=not args.no_warm)
+            m2 = measure(w2, steps, max(10, args.warmup // 4), warm=not args.no_warm,
+                         alt=not args.no_alt)
             progress(f"{name}: graph {m2['graph_wall'] / steps * 1e3:.4f} ms/step, kernels "
                      f"{m2['kern_ms']}")
             extra[name] = dict(value=round(w2.sampled_rows * steps / m2["graph_wall"], 1),
