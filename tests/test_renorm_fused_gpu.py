@@ -67,14 +67,18 @@ def compare_renormalised(g, o, x, top_n, lists, tag=""):
         assert (a == b) if np.isinf(b) else abs(a - b) <= 1e-5, (tag, r, a, b)
 
 
-def check(x, params, top_n, lists, tag, mask_lists=None, xd=None):
+def check(x, params, top_n, lists, tag, mask_lists=None, xd=None, history=None, hist_len=None,
+          **kw):
     say("case renorm", tag, np.asarray(x).shape, "top_n", top_n)
     xd = to_dev(np.asarray(x, np.float32)) if xd is None else xd
-    g = gpu_call(xd, params, top_n, lists, mask_lists)
+    if history is not None:
+        kw.update(history=to_dev(np.asarray(history, np.int32)), history_len=hist_len)
+    g = gpu_call(xd, params, top_n, lists, mask_lists, **kw)
     if mask_lists is None:
-        o = O.sample_tokens(np.asarray(x, np.float32), params)
+        o = O.sample_tokens(np.asarray(x, np.float32), params, history, hist_len)
     else:
-        o = O.sample_tokens_masked(np.asarray(x, np.float32), params, mask_lists)
+        o = O.sample_tokens_masked(np.asarray(x, np.float32), params, mask_lists, history,
+                                   hist_len)
     compare_sample(g, o, tag)
     compare_fused_logprobs(g, o, x, top_n, tag + " unrestricted")
     compare_renormalised(g, o, x, top_n, lists, tag + " renormalised")
@@ -149,6 +153,35 @@ def test_longest_fused_list_and_the_first_longer_one(n):
     lists = [rng.choice(V, n, replace=False).astype(np.int32) for _ in range(4)]
     lists[2] = np.zeros(0, np.int32)
     check(x, params, 20, lists, f"list of {n}")
+
+
+def test_penalised_rows():
+    """Penalties force the second (raw) selection, merged in the same tail
+    that meets the renormalising workgroup."""
+    w = W.batch_slots()
+    rng = np.random.default_rng(39)
+    lists = mixed_lists(rng, V, len(w["params"]))
+    check(w["logits"], w["params"], 20, lists, "penalised renorm", history=w["history"],
+          hist_len=w["hist_len"])
+
+
+def test_verify_windows():
+    """Windows of five rows with drafts: acceptance and renormalised logprobs
+    from one launch."""
+    rng = np.random.default_rng(40)
+    B, window = 10, 5
+    x = rng.normal(0, 3, (B, V)).astype(np.float32)
+    params = [sampled(top_k=40, top_p=0.95, counter=r) for r in range(B)]
+    o = O.sample_tokens(x, params)
+    drafts = o["token"].astype(np.int32).copy()
+    drafts[2] = (drafts[2] + 1) % V          # window 0 accepts two rows
+    lists = mixed_lists(rng, V, B)
+    g, o2 = check(x, params, 20, lists, "windows renorm", window=window, draft=to_dev(drafts))
+    want = O.accept_windows(o2["token"], window, drafts)
+    for w in range(B // window):
+        rows = slice(w * window, (w + 1) * window)
+        if np.array_equal(g["token"][rows], o2["token"][rows]):
+            assert g["accepted"][w] == want[w], (w, g["accepted"][w], want[w])
 
 
 def test_masked_rows_take_the_separate_pass():
