@@ -29,7 +29,7 @@ struct SampleSmem {
     uint32_t pen_cnt[(LP && EPT * kBlock / 2 < kRenormSlots) ? kRenormSlots : EPT * kBlock / 2];
     uint64_t raw_keys[LP ? 4 * kRegion : 1];  // candidates of the raw top-K
     uint32_t raw_cnt[4];
-    uint32_t lpa_member[2];  // the sampled token is in the row's allowed list (waves 2, 3)
+    uint32_t lpa_member[4];  // the sampled token is in the row's allowed list (per wave)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -105,6 +105,12 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // them.  Ids past V read as NaN: never selected.
     float v[EPT];
     load_chunk<EPT, VEC>(x, base, V, v);
+    // A row renormalised over an allowed list: the workgroups of its first
+    // eight chunks (one per XCD) touch every line of the list, so the row's
+    // merging workgroup finds it in its XCD's L2.
+    int32_t pf = 0;
+    if (LP && (R.pack & kPackRenorm) != 0u && chunk < 8 && tid * 32 < R.allowed_cnt)
+        pf = a.allowed[R.allowed_off + tid * 32];
 
     // Raw-logit logprobs in the same pass (page "#3200 ...", "Approach": the
     // reported distribution is taken before penalties and temperature): the
@@ -122,6 +128,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     uint64_t *raw_out = LP ? a.raw_keys + (int64_t)slot * a.raw_stride + (int64_t)chunk * K : nullptr;
     bool raw_done = false;
     if (LP) {
+        // keeps the prefetch load (its value is unused); the wait for it is
+        // the wait for the chunk's own loads, issued before it
+        asm volatile("" ::"v"(pf));
         const float2 lms = lane_max_sum<EPT>(v, [&]() {
             // ids below V among the lane's groups of four
             int c = 0;
@@ -229,7 +238,20 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // computed while the merge's first loads are in flight.
     const uint64_t ctr = a.counters ? a.counters[slot] : R.counter;
     uint32_t x0 = 0u;
+    // A row renormalised over an allowed list: its ids load once the merge's
+    // first loads are issued, so the merge hides their latency; the tail
+    // looks the drawn token up in them.
+    const bool renorm = LP && (R.pack & kPackRenorm) != 0u;
+    int32_t al[kRenormPerThread];
     list_topk(sm.s, list, a.nchunks, k, [&]() {
+        if (renorm) {
+            const int32_t *ids = a.allowed + R.allowed_off;
+#pragma unroll
+            for (int j = 0; j < kRenormPerThread; ++j) {
+                const int f = tid + j * kBlock;
+                al[j] = f < R.allowed_cnt ? ids[f] : -1;
+            }
+        }
         if (!greedy) x0 = philox4x32_10_x0(ctr, R.seed);
     });
 
@@ -242,10 +264,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // ---- with raw logprobs: wave 0 loads the raw logit of every kept id
     // (the token is one of them) and runs the cuts and the draw while wave 1
     // combines the chunk partials; neither waits for the other's loads.  On a
-    // row renormalised over an allowed list, waves 2 and 3 load the list
-    // meanwhile, and wave 0 meets the row's renormalising workgroup (see
-    // rts_renorm.h) once the token is published.
-    const bool renorm = (R.pack & kPackRenorm) != 0u;
+    // row renormalised over an allowed list, every wave then looks the token
+    // up in the list ids it loaded during the merge, and wave 0 meets the
+    // row's renormalising workgroup (see rts_renorm.h).
     uint64_t *const lpa_w = a.lpa_w + (int64_t)slot * (kTicketStride / 2);
     float xt = 0.0f;      // wave 0: the sampled token's raw logit
     uint64_t enc = 0ull;  // wave 0, lane 0: the renormalising workgroup's enc(L), 0 if not done
@@ -268,21 +289,17 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
             sm.s.red[0] = (uint64_t)__double_as_longlong(L1);
             sm.s.red[1] = u1 ? 1ull : 0ull;
         }
-    } else if (renorm) {
-        // the list into LDS (the penalty counts' space, free by now)
-        const int32_t *ids = a.allowed + R.allowed_off;
-        for (int f = tid - 128; f < R.allowed_cnt; f += 128)
-            sm.pen_cnt[f] = (uint32_t)ids[f];
     }
     __syncthreads();
     const double L = __longlong_as_double((long long)sm.s.red[0]);
     const bool uniform = sm.s.red[1] != 0ull;
-    if (renorm && wave >= 2) {
+    if (renorm) {
         const int32_t t = (int32_t)sm.s.flag;
         bool hit = false;
-        for (int f = tid - 128; f < R.allowed_cnt; f += 128) hit = hit || ((int32_t)sm.pen_cnt[f] == t);
+#pragma unroll
+        for (int j = 0; j < kRenormPerThread; ++j) hit = hit || (al[j] == t);
         const uint64_t b = __ballot(hit && t >= 0 && t < V);
-        if (lane == 0) sm.lpa_member[wave - 2] = b ? 1u : 0u;
+        if (lane == 0) sm.lpa_member[wave] = b ? 1u : 0u;
     }
     __syncthreads();  // the raw merge below may reuse sm.red
     if (raw_sel) list_topk(sm.s, a.raw_keys + (int64_t)slot * a.raw_stride, a.nchunks, K);
@@ -296,7 +313,8 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         if (lpa_copy) a.lpa_token[slot] = lp;
         if (renorm && enc != 0ull) {
             // the renormalising workgroup finished first: this one writes
-            const bool member = (sm.lpa_member[0] | sm.lpa_member[1]) != 0u;
+            const bool member =
+                (sm.lpa_member[0] | sm.lpa_member[1] | sm.lpa_member[2] | sm.lpa_member[3]) != 0u;
             a.lpa_token[slot] = renorm_token_lp(enc, member, xt);
             publish_u64(lpa_w, 0ull);
         }
