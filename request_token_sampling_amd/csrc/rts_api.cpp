@@ -431,6 +431,8 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
             a.lpa_token = lp->allowed_token_lp + r0;
             a.lpa_ids = lp->top_n > 0 ? lp->allowed_top_ids + r0 * lp->top_n : nullptr;
             a.lpa_top = lp->top_n > 0 ? lp->allowed_top_lp + r0 * lp->top_n : nullptr;
+            // the first 8 bytes of each logprob ticket line: the row's exchange
+            // word (zero between calls, like the tickets)
             a.lpa_w = reinterpret_cast<uint64_t *>(ws + rts::kTicketRegion);
             if (lpa_fused && lpa_max > 0) {
                 a.allowed = lpa;
