@@ -127,3 +127,22 @@ def compare_fused_logprobs(g, o, logits, top_n, tag=""):
         assert t in table, (tag, r, "token outside the kept ids")
         assert abs(float(g["token_lp"][r]) - table[t]) <= LP_ATOL, (tag, r, "token_lp")
     return int(np.sum(~same))
+
+
+def compare_renormalised(g, o, x, top_n, lists, tag=""):
+    """The renormalised outputs against the oracle's for the oracle's tokens;
+    where the GPU drew another kept id (a flagged row), its logprob is looked
+    up in the oracle's values for every kept id."""
+    ol = O.token_logprobs(x, o["token"], top_n, lists)
+    same = g["token"] == o["token"]
+    gl = dict(token_lp=np.where(same, g["allowed_token_lp"], ol["token_lp"]),
+              top_ids=g["allowed_top_ids"], top_lp=g["allowed_top_lp"])
+    compare_logprobs(gl, ol, tag)
+    for r in np.nonzero(~same)[0]:
+        k = int(o["counts"][r, 0])
+        table = {int(i): O.token_logprobs_row(x[r], int(i), 0, lists[r])["token_lp"]
+                 for i in o["kept_ids"][r][:k]}
+        t = int(g["token"][r])
+        assert t in table, (tag, r, "token outside the kept ids")
+        a, b = float(g["allowed_token_lp"][r]), table[t]
+        assert (a == b) if np.isinf(b) else abs(a - b) <= LP_ATOL, (tag, r, a, b)

@@ -14,7 +14,8 @@ import oracle.oracle as O
 import request_token_sampling_amd as R
 from request_token_sampling_amd import workloads as W
 
-from parity import compare_fused_logprobs, compare_logprobs, compare_sample, say, to_dev
+from parity import (compare_fused_logprobs, compare_logprobs, compare_renormalised,
+                    compare_sample, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -142,6 +143,61 @@ def test_random_logprob_configuration(seed):
     g = {k: v.cpu().numpy() for k, v in out.items()}
     o = O.token_logprobs(x, tokens, top_n, lists)
     compare_logprobs(g, o, f"random logprobs {seed}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_renormalised_configuration(seed):
+    """Sampling calls that also renormalise their logprobs over allowed
+    lists: lists of random length (past 2,048 ids some rows take the
+    separate pass), repeats and foreign ids, sometimes with candidate masks
+    on other rows (separate pass), penalties, broadcast rows."""
+    rng = np.random.default_rng(11000 + seed)
+    B = int(rng.choice([1, 2, 5, 17, 40, 70]))
+    V = int(rng.choice([7, 100, 1023, 4097, 30011, 120000]))
+    broadcast = B > 1 and rng.random() < 0.25
+    x, kind = _logits(rng, 1 if broadcast else B, V)
+    xs = np.repeat(x, B, axis=0) if broadcast else x
+    H = int(rng.integers(0, 3))
+    hist = rng.integers(-2, V + 2, (H, 200)).astype(np.int32) if H else None
+    hist_len = [int(rng.integers(0, 201)) for _ in range(H)] if H else None
+    params = _params(rng, B, H, V)
+    top_n = int(rng.choice([0, 1, 5, 20]))
+    lists = []
+    for r in range(B):
+        u = rng.random()
+        if u < 0.2:
+            lists.append(None)
+        elif u < 0.85:
+            lists.append(rng.integers(-3, V + 3, int(rng.integers(0, 700))).astype(np.int32))
+        else:
+            lists.append(rng.integers(-3, V + 3, int(rng.integers(1900, 2300))).astype(np.int32))
+    masks = None
+    if rng.random() < 0.2:
+        masks = [None] * B
+        masks[int(rng.integers(0, B))] = rng.integers(0, V, 30).astype(np.int32)
+    say("case random renorm", seed, dict(B=B, V=V, kind=kind, broadcast=broadcast, H=H,
+                                         top_n=top_n, masks=masks is not None,
+                                         longest=max((0 if a is None else a.size) for a in lists)))
+    xd = to_dev(x)
+    view = xd.expand(B, -1) if broadcast else xd
+    hd = None if hist is None else to_dev(hist)
+    ids, off = W.pack_allowed(lists)
+    kw = dict(logprob_allowed=to_dev(ids) if ids.size else torch.zeros(1, dtype=torch.int32,
+                                                                       device="cuda"),
+              logprob_allowed_off=off)
+    if masks is not None:
+        mids, moff = W.pack_allowed(masks)
+        kw.update(allowed=to_dev(mids), allowed_off=moff)
+    out = R.sample_tokens(view, params, hd, hist_len, logprobs=top_n, **kw)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    if masks is not None:
+        o = O.sample_tokens_masked(xs, params, masks, hist, hist_len)
+    else:
+        o = O.sample_tokens(xs, params, hist, hist_len)
+    compare_sample(g, o, f"random renorm {seed}")
+    compare_fused_logprobs(g, o, xs, top_n, f"random renorm {seed} logprobs")
+    compare_renormalised(g, o, xs, top_n, lists, f"random renorm {seed} renormalised")
 
 
 @pytest.mark.parametrize("seed", range(12))

@@ -18,7 +18,7 @@ import oracle.oracle as O
 import request_token_sampling_amd as R
 from request_token_sampling_amd import workloads as W
 
-from parity import compare_fused_logprobs, compare_logprobs, compare_sample, say, to_dev
+from parity import compare_fused_logprobs, compare_renormalised, compare_sample, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -46,25 +46,6 @@ def gpu_call(xd, params, top_n, lists, mask_lists=None, **kw):
                           logprob_allowed_off=off, **kw)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
-
-
-def compare_renormalised(g, o, x, top_n, lists, tag=""):
-    """The renormalised outputs against the oracle's for the oracle's tokens;
-    where the GPU drew another kept id (a flagged row), its logprob is looked
-    up in the oracle's values for every kept id."""
-    ol = O.token_logprobs(x, o["token"], top_n, lists)
-    same = g["token"] == o["token"]
-    gl = dict(token_lp=np.where(same, g["allowed_token_lp"], ol["token_lp"]),
-              top_ids=g["allowed_top_ids"], top_lp=g["allowed_top_lp"])
-    compare_logprobs(gl, ol, tag)
-    for r in np.nonzero(~same)[0]:
-        k = int(o["counts"][r, 0])
-        table = {int(i): O.token_logprobs_row(x[r], int(i), 0, lists[r])["token_lp"]
-                 for i in o["kept_ids"][r][:k]}
-        t = int(g["token"][r])
-        assert t in table, (tag, r, "token outside the kept ids")
-        a, b = float(g["allowed_token_lp"][r]), table[t]
-        assert (a == b) if np.isinf(b) else abs(a - b) <= 1e-5, (tag, r, a, b)
 
 
 def check(x, params, top_n, lists, tag, mask_lists=None, xd=None, history=None, hist_len=None,
