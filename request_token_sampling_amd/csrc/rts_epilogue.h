@@ -7,6 +7,8 @@
 
 namespace rts {
 
+constexpr int kPackedWindow = 33;  // windows this long or shorter take window_step_packed
+
 // llama.cpp-style penalty of an id seen c > 0 times in the window: the repeat
 // penalty divides a positive logit and multiplies a non-positive one, the
 // frequency term scales with the count and the presence term is charged once.
@@ -24,9 +26,35 @@ __device__ __forceinline__ float penalize(float v, uint32_t c, float rep, float 
 // Verify windows (page "#19 ...", "What changed": the emitted tokens are the
 // target's own samples; page "#559 ...", "Not done (yet)": a sampled row is
 // accepted when its pick equals the draft).  Run by wave 0 of a row's merging
-// workgroup once the row's token is published: the window's last row to get
-// here counts the leading rows whose token equals their draft and writes the
-// number of tokens the window emits.
+// workgroup once the row's token is known: the window's last row to get here
+// counts the leading rows whose token equals their draft and writes the
+// number of tokens the window emits (the first mismatch among all rows but
+// the last, plus one; the window's size when there is none).
+//
+// Windows of up to 33 rows: each row adds 2^32 (one arrival) plus, if its
+// token equals its draft, 2^r (r its place; the last row's bit is never
+// read) to the window's 64-bit word with one device-scope atomic, so the
+// last arrival reads every row's outcome from the value the atomic returns;
+// no token is published and nothing else is read.
+__device__ __forceinline__ void window_step_packed(const SampleArgs &a, int slot, int32_t tok,
+                                                   int32_t draft)
+{
+    if (lane_id() != 0) return;
+    const int w = slot / a.window, r = slot - w * a.window;
+    const uint64_t add = (1ull << 32) | ((r < a.window - 1 && tok == draft) ? (1ull << r) : 0ull);
+    uint64_t *word = reinterpret_cast<uint64_t *>(&a.wtickets[w * kTicketStride]);
+    const uint64_t old =
+        __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((old >> 32) != (uint64_t)(a.window - 1)) return;
+    const uint32_t rows = (uint32_t)(a.window - 1);  // rows whose match decides
+    const uint32_t span = rows >= 32u ? 0xFFFFFFFFu : ((1u << rows) - 1u);
+    const uint32_t miss = ~(uint32_t)(old + add) & span;
+    a.accepted[w] = miss ? __ffs(miss) : a.window;
+    publish_u64(word, 0ull);  // ready for the next launch on this workspace
+}
+
+// Longer windows: the row's token is published, then a ticket, and the last
+// row reads every row's token back.
 __device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32_t tok)
 {
     const int lane = lane_id();
@@ -58,6 +86,8 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
                                          int slot, int k, bool greedy, uint64_t ctr, uint32_t x0)
 {
     const int lane = lane_id();
+    // a verify window's draft for this row, loaded now so the cuts hide it
+    const int32_t draft = (a.window > 0 && a.window <= kPackedWindow) ? a.draft[slot] : 0;
     const uint64_t key = (lane < k) ? sm.sel[lane] : 0ull;
     const bool valid = key != 0ull;
     const int32_t id = valid ? (int32_t)key_index(key) : -1;
@@ -111,7 +141,7 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     const int32_t tok = lane_i32(id, pick);
     if (lane == 0) {
         sm.flag = (uint32_t)tok;
-        if (a.window > 0) publish_i32(&a.token[slot], tok);  // read by the window's last row
+        if (a.window > kPackedWindow) publish_i32(&a.token[slot], tok);  // read by the window's last row
         else a.token[slot] = tok;
         if (a.counts) {
             a.counts[3 * (int64_t)slot + 0] = k;
@@ -122,7 +152,8 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
         if (a.counters) a.counters[slot] = ctr + (uint64_t)a.counter_stride;
         a.tickets[slot * kTicketStride] = 0u;  // ready for the next launch on this workspace
     }
-    if (a.window > 0) window_step(a, slot, tok);
+    if (a.window > kPackedWindow) window_step(a, slot, tok);
+    else if (a.window > 0) window_step_packed(a, slot, tok, draft);
 }
 
 }  // namespace rts

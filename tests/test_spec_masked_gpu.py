@@ -106,7 +106,8 @@ def windows_case(B, window, seed):
     return x, params, o, drafts
 
 
-@pytest.mark.parametrize("B,window", [(5, 5), (75, 5), (12, 1), (64, 64), (30, 3)])
+@pytest.mark.parametrize("B,window", [(5, 5), (75, 5), (12, 1), (64, 64), (30, 3), (66, 33),
+                                      (68, 34)])
 def test_verify_window_acceptance(B, window):
     x, params, o, drafts = windows_case(B, window, B * 100 + window)
     say("case windows", B, window)
