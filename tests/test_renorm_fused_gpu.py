@@ -136,6 +136,18 @@ def test_longest_fused_list_and_the_first_longer_one(n):
     check(x, params, 20, lists, f"list of {n}")
 
 
+def test_vocabulary_past_the_standalone_limit():
+    """Lists renormalised inside the sampling call need no vocabulary bitmap,
+    so V may exceed 2^19 (the stand-alone kernels' limit)."""
+    rng = np.random.default_rng(41)
+    Vx = 1_100_003
+    x = rng.normal(0, 3, (2, Vx)).astype(np.float32)
+    params = [sampled(top_k=20, counter=0), W.row_params()]
+    lists = [rng.choice(Vx, 1500, replace=False).astype(np.int32),
+             np.concatenate([[int(np.argmax(x[1]))], rng.integers(0, Vx, 600)]).astype(np.int32)]
+    check(x, params, 20, lists, "V past 2^19")
+
+
 def test_penalised_rows():
     """Penalties force the second (raw) selection, merged in the same tail
     that meets the renormalising workgroup."""
