@@ -39,6 +39,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+CONSUMER_SRC = os.path.join(ROOT, "tests", "c_abi_consumer.cpp")
+CONSUMER = os.path.join(ROOT, "tests", "_build", "c_abi_consumer")
+
+
+def build_consumer(verbose: bool = False) -> str:
+    """The plain C++ program in tests/ that uses the library through
+    include/rts.h and the HIP runtime alone, linked to the in-tree librts.so."""
+    os.makedirs(os.path.dirname(CONSUMER), exist_ok=True)
+    tmp = CONSUMER + ".tmp"
+    cmd = ["/opt/rocm/bin/hipcc", "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, CONSUMER_SRC,
+           "-o", tmp, "-L", HERE, "-lrts", "-Wl,-rpath,$ORIGIN/../../request_token_sampling_amd",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, CONSUMER)
+    return CONSUMER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_consumer(verbose=True))
     sys.exit(0)
