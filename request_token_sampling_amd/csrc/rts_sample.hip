@@ -101,8 +101,14 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     const int base = chunk * CH;
     const float *x = a.logits + (int64_t)slot * a.ld;
 
-    // Issue every load of the chunk first; the bitmap build below overlaps
-    // them.  Ids past V read as NaN: never selected.
+    // Each thread's first history id is loaded before the chunk: loads return
+    // in order, so one issued after the chunk's could only be used once the
+    // whole chunk had arrived, and the bitmap build below could not overlap
+    // the chunk's loads.  (The fused-logprob variant reads its chunk before
+    // the penalties and keeps the plain order.)
+    const int32_t *h = a.history + R.hist_off;
+    const int32_t h0 = (!LP && n_eff > 0 && tid < n_eff) ? h[tid] : -1;
+    // Then every load of the chunk.  Ids past V read as NaN: never selected.
     float v[EPT];
     load_chunk<EPT, VEC>(x, base, V, v);
     // A row renormalised over an allowed list: the workgroups of its first
@@ -153,10 +159,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     if (n_eff > 0) {
         // Clear the chunk's bits and only the count words the window touches.
         for (int w = tid; w < CH / 32; w += kBlock) sm.pen_bits[w] = 0u;
-        const int32_t *h = a.history + R.hist_off;
         uint32_t bad = 0;
         for (int j = tid; j < n_eff; j += kBlock) {
-            const int32_t id = h[j];
+            const int32_t id = (!LP && j == tid) ? h0 : h[j];
             const int rel = id - base;
             if (id >= 0 && id < V && rel >= 0 && rel < CH) sm.pen_cnt[rel >> 1] = 0u;
             bad += (id < 0 || id >= V) ? 1u : 0u;
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         if (count_ignored && bad) atomicAdd(a.ignored, bad);
         __syncthreads();
         for (int j = tid; j < n_eff; j += kBlock) {
-            const int32_t id = h[j];
+            const int32_t id = (!LP && j == tid) ? h0 : h[j];
             const int rel = id - base;
             if (id >= 0 && id < V && rel >= 0 && rel < CH) {
                 atomicOr(&sm.pen_bits[rel >> 5], 1u << (rel & 31));
