@@ -158,22 +158,25 @@ int check_offsets(int64_t B, const int64_t *off, const char *what)
     return RTS_OK;
 }
 
-// The allowed-id logprob kernels keep a vocabulary bitmap in LDS: sets
-// *fast_fits when the gather-once kernel's LDS fits too.
+// Allowed lists longer than kRenormMax ids take the bitmap kernels, which keep a
+// vocabulary bitmap in LDS: sets *fast_fits when the gather-once kernel's LDS
+// fits too.
 int check_allowed_lds(int64_t V, bool *fast_fits)
 {
     const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
     const size_t max_lds = V > (1 << 19) ? 0 : max_lds_per_block();
     if (bitmap_bytes + rts::kAllowedStaticLds > max_lds)
-        return fail(RTS_EINVAL, "allowed lists need V <= 2^19 (V = %lld)", (long long)V);
+        return fail(RTS_EINVAL, "allowed lists of more than %d ids need V <= 2^19 (V = %lld)",
+                    rts::kRenormMax, (long long)V);
     *fast_fits = bitmap_bytes + rts::kAllowedStaticLds <= max_lds;
     return RTS_OK;
 }
 
 // The launches of rts_token_logprobs once its arguments are checked.  Rows
 // with an empty list take the full-row reducer, unless `restricted_only`
-// leaves them out; short lists take the gather-once kernel, longer ones the
-// bitmap-walking kernel.  ld = 0 makes every row read row 0.
+// leaves them out; lists of up to kRenormMax ids the hash-set kernel; longer
+// ones the bitmap kernels (gather-once up to kAllowedFast ids, else walking).
+// ld = 0 makes every row read row 0.
 int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, const int32_t *tokens,
                      int32_t top_n, const int32_t *allowed, const int64_t *allowed_off,
                      float *token_lp, int32_t *top_ids, float *top_lp, void *workspace,
@@ -205,9 +208,9 @@ int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, cons
     base.top_n = top_n;
     base.partials = reinterpret_cast<float2 *>(ws + L.partials);
 
-    // kind 0: unrestricted rows (full-row reducer); 1: short lists; 2: long lists.
-    // Each kind in launches of up to 64 rows.
-    for (int kind = restricted_only ? 1 : 0; kind < 3; ++kind) {
+    // kind 0: unrestricted rows (full-row reducer); then rts::kAllowedHash,
+    // kAllowedFastBitmap and kAllowedWide.  Each kind in launches of up to 64 rows.
+    for (int kind = restricted_only ? 1 : 0; kind <= rts::kAllowedWide; ++kind) {
         if (kind > 0 && !any_restricted) break;
         rts::LogprobArgs a = base;
         int n = 0;
@@ -223,14 +226,17 @@ int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, cons
                 a.early_xcds = n * a.nchunks <= rts::kEarlyXcdWork ? 1 : 0;
                 e = rts::launch_logprobs_full(a, ept, vec, stream);
             } else {
-                e = rts::launch_logprobs_allowed(a, bitmap_bytes, kind == 2, stream);
+                e = rts::launch_logprobs_allowed(a, bitmap_bytes, kind, stream);
             }
             n = 0;
             return e;
         };
         for (int64_t r = 0; r < B; ++r) {
             const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
-            const int row_kind = cnt == 0 ? 0 : ((fast_fits && cnt <= rts::kAllowedFast) ? 1 : 2);
+            const int row_kind = cnt == 0                  ? 0
+                                 : cnt <= rts::kRenormMax ? rts::kAllowedHash
+                                 : (fast_fits && cnt <= rts::kAllowedFast) ? rts::kAllowedFastBitmap
+                                                                           : rts::kAllowedWide;
             if (row_kind != kind) continue;
             rts::LogprobRow &lr = a.row[n++];
             lr.row = (int32_t)r;
@@ -367,7 +373,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
         for (int64_t r = 0; r < B; ++r)
             if (lpa_off[r + 1] - lpa_off[r] > lpa_max) lpa_max = lpa_off[r + 1] - lpa_off[r];
         lpa_fused = allowed == nullptr && lpa_max <= rts::kRenormMax && lpa_off[B] <= 0x7FFFFFFFLL;
-        if (!lpa_fused && lpa_max > 0)
+        if (!lpa_fused && lpa_max > rts::kRenormMax)
             if (const int e = check_allowed_lds(V, &lpa_fast)) return e;
     }
 
@@ -489,15 +495,14 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (ws_bytes < need)
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
-    // Restricted rows take the gather-once kernel when their list is short
-    // enough, else the bitmap-walking kernel; both keep a vocabulary bitmap
-    // in LDS.
-    bool any_restricted = false, fast_fits = false;
+    // Restricted rows: lists of up to kRenormMax ids take the hash-set kernel
+    // (any V); longer ones the bitmap kernels, which need V <= 2^19.
+    bool any_long = false, fast_fits = false;
     if (allowed != nullptr) {
         if (const int e = check_offsets(B, allowed_off, "allowed_off")) return e;
         for (int64_t r = 0; r < B; ++r)
-            if (allowed_off[r + 1] > allowed_off[r]) any_restricted = true;
-        if (any_restricted)
+            if (allowed_off[r + 1] - allowed_off[r] > rts::kRenormMax) any_long = true;
+        if (any_long)
             if (const int e = check_allowed_lds(V, &fast_fits)) return e;
     }
     return enqueue_logprobs(logits, B, V, ld, tokens, top_n, allowed, allowed_off, token_lp, top_ids,

@@ -183,7 +183,12 @@ __host__ __device__ inline int sample_work(int rows, int nchunks, int early, int
 // Launchers (return a hipError_t as int).
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
 int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s);
-int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s);
+// Kernels for restricted rows: a hash set (lists of <= kRenormMax ids, any V),
+// or a vocabulary bitmap gathering at once (<= kAllowedFast ids) or walking it.
+constexpr int kAllowedHash = 1;
+constexpr int kAllowedFastBitmap = 2;
+constexpr int kAllowedWide = 3;
+int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, int kind, hipStream_t s);
 int launch_zero_u32(uint32_t *p, size_t n, hipStream_t s);
 
 // The pages' earlier designs (rts_sample_tokens_prior): one thread per row,

@@ -13,12 +13,13 @@
 // keys (rts_select.h), and publishes one (max, sum) pair and K keys.  The
 // last workgroup of the row combines the pairs in fp64 in chunk order and
 // merges the keys.
-// Restricted rows: one workgroup per row and an LDS bitmap of the vocabulary,
-// so duplicates count once and foreign ids are ignored.  Lists of up to
-// kAllowedFast ids are gathered at once into registers, the thread that sets
-// an id's bit owning it; longer lists are marked first and the set bits
+// Restricted rows: one workgroup per row.  Lists of up to kRenormMax ids
+// drop repeats and foreign ids with a hash set in LDS (rts_renorm.h), for any
+// V.  Longer lists use an LDS bitmap of the vocabulary (V <= 2^19): lists of
+// up to kAllowedFast ids are gathered at once into registers, the thread that
+// sets an id's bit owning it; longer ones are marked first and the set bits
 // walked, so each member is gathered exactly once.
-#include "rts_select.h"
+#include "rts_renorm.h"
 
 namespace rts {
 
@@ -419,9 +420,47 @@ int launch_logprobs_full(const LogprobArgs &a, int ept, bool vec, hipStream_t s)
     }
 }
 
-int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, bool wide, hipStream_t s)
+// One workgroup per restricted row with at most kRenormMax listed ids.
+__global__ __launch_bounds__(kBlock) void logprob_allowed_hash_kernel(const LogprobArgs a)
 {
-    if (wide)
+    __shared__ SelectSmem sm;
+    __shared__ uint32_t tab[kRenormSlots];
+    __shared__ uint32_t s_member;
+
+    const int tid = threadIdx.x;
+    const LogprobRow R = a.row[blockIdx.x];
+    const int row = R.row;
+    const int V = a.V;
+    const int K = a.top_n;
+    const float *x = a.logits + (int64_t)row * a.ld;
+    // the token and its logit, loaded now so their latency hides behind the rest
+    const int32_t t = a.tokens[row];
+    const bool tv = t >= 0 && t < V;
+    const float xt = (tid == 0 && tv) ? x[t] : 0.0f;
+    if (tid == 0) s_member = 0u;  // ordered before its use by the barriers below
+    int32_t id[kRenormPerThread];
+    double L;
+    bool uniform;
+    allowed_members(sm, tab, x, a.allowed + R.allowed_off, (int)R.allowed_cnt, V, K,
+                    K > 0 ? a.top_ids + (int64_t)row * K : nullptr,
+                    K > 0 ? a.top_lp + (int64_t)row * K : nullptr, id, L, uniform);
+    bool hit = false;
+#pragma unroll
+    for (int j = 0; j < kRenormPerThread; ++j) hit = hit || (id[j] == t);
+    if (tv && hit) s_member = 1u;
+    __syncthreads();
+    if (tid == 0) {
+        float lp = -INFINITY;
+        if (s_member != 0u) lp = uniform ? (float)(-L) : (float)((double)sanitize(xt) - L);
+        a.token_lp[row] = lp;
+    }
+}
+
+int launch_logprobs_allowed(const LogprobArgs &a, size_t lds_bytes, int kind, hipStream_t s)
+{
+    if (kind == kAllowedHash)
+        hipLaunchKernelGGL(logprob_allowed_hash_kernel, dim3((unsigned)a.rows), dim3(kBlock), 0, s, a);
+    else if (kind == kAllowedWide)
         hipLaunchKernelGGL(logprob_allowed_wide_kernel, dim3((unsigned)a.rows), dim3(kBlock),
                            (unsigned)lds_bytes, s, a);
     else

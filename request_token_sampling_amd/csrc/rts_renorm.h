@@ -62,26 +62,22 @@ __device__ __forceinline__ uint32_t renorm_hash(uint32_t id)
 }
 static_assert(kRenormSlots == 1 << 12, "renorm_hash yields 12 bits");
 
-// The renormalising workgroup of row `slot`.  `tab` is kRenormSlots words of
-// LDS besides `sm`.  Rows without kPackRenorm exit.
-// Every member term of the sum is rounded to a multiple of 2^-40 before it
-// is added, so the fp64 sum does not depend on which thread owns a repeated
-// id: the result equals rts_token_logprobs' for the same list.
-__device__ __forceinline__ void renorm_block(const SampleArgs &a, SelectSmem &sm, uint32_t *tab,
-                                             int slot)
+// Logprobs over one allowed list, by one workgroup: the listed ids and their
+// logits are gathered at once (kRenormPerThread per thread, cnt <= kRenormMax),
+// repeats and ids outside [0, V) dropped with a hash set of kRenormSlots words
+// in `tab` (LDS), then L = log sum exp over the members (log of the member
+// count when every member is -inf; +inf when there is none) and the top-K
+// members, written to top_ids / top_lp when K > 0.  Every member term of the
+// sum is rounded to a multiple of 2^-40 before it is added, so the fp64 sum
+// does not depend on which thread owns a repeated id.  Leaves each thread's
+// listed ids in id[] (-1 past the list) and ends after a barrier.
+__device__ __forceinline__ void allowed_members(SelectSmem &sm, uint32_t *tab, const float *x,
+                                                const int32_t *ids, int cnt, int V, int K,
+                                                int32_t *top_ids, float *top_lp,
+                                                int32_t (&id)[kRenormPerThread], double &L_out,
+                                                bool &uniform_out)
 {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    if (slot >= a.rows) return;
-    const SampleRow R = a.row[slot];
-    if ((R.pack & kPackRenorm) == 0u) return;
-    const int V = a.V;
-    const int K = a.lp_topn;
-    const int cnt = R.allowed_cnt;  // 1..kRenormMax (host-checked)
-    const float *x = a.logits + (int64_t)slot * a.ld;
-    const int32_t *ids = a.allowed + R.allowed_off;
-
-    // the listed ids and their logits, every load in flight together
-    int32_t id[kRenormPerThread];
     float v[kRenormPerThread];
 #pragma unroll
     for (int j = 0; j < kRenormPerThread; ++j) {
@@ -115,8 +111,6 @@ __device__ __forceinline__ void renorm_block(const SampleArgs &a, SelectSmem &sm
         mine += owner ? 1u : 0u;
     }
 
-    // L = M + log(sum exp(x - M)) over the members (log of the member count
-    // when every member is -inf; +inf when there is none)
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < kRenormPerThread; ++j) lmax = (v[j] == v[j]) ? fmaxf(lmax, v[j]) : lmax;
@@ -146,6 +140,8 @@ __device__ __forceinline__ void renorm_block(const SampleArgs &a, SelectSmem &sm
     const bool empty = members == 0u;
     const bool uniform = !empty && Mf == -INFINITY;
     const double L = empty ? INFINITY : (uniform ? log(S) : M + log(S));
+    L_out = L;
+    uniform_out = uniform;
 
     if (K > 0) {
         // top-K members: lane maxima -> threshold -> compaction -> rank
@@ -193,11 +189,33 @@ __device__ __forceinline__ void renorm_block(const SampleArgs &a, SelectSmem &sm
         if (tid < K) {
             const uint64_t key = sm.sel[tid];
             const bool valid = key != 0ull;
-            a.lpa_ids[(int64_t)slot * K + tid] = valid ? (int32_t)key_index(key) : -1;
-            a.lpa_top[(int64_t)slot * K + tid] =
+            top_ids[tid] = valid ? (int32_t)key_index(key) : -1;
+            top_lp[tid] =
                 valid ? (uniform ? (float)(-L) : (float)((double)key_logit(key) - L)) : -INFINITY;
         }
     }
+    __syncthreads();
+}
+
+// The renormalising workgroup of row `slot` in a sampling launch.  `tab` is
+// kRenormSlots words of LDS besides `sm`.  Rows without kPackRenorm exit.
+// Its results equal rts_token_logprobs' for the same list.
+__device__ __forceinline__ void renorm_block(const SampleArgs &a, SelectSmem &sm, uint32_t *tab,
+                                             int slot)
+{
+    const int tid = threadIdx.x;
+    if (slot >= a.rows) return;
+    const SampleRow R = a.row[slot];
+    if ((R.pack & kPackRenorm) == 0u) return;
+    const int V = a.V;
+    const int K = a.lp_topn;
+    const float *x = a.logits + (int64_t)slot * a.ld;
+    int32_t id[kRenormPerThread];
+    double L;
+    bool uniform;
+    allowed_members(sm, tab, x, a.allowed + R.allowed_off, R.allowed_cnt, V, K,
+                    K > 0 ? a.lpa_ids + (int64_t)slot * K : nullptr,
+                    K > 0 ? a.lpa_top + (int64_t)slot * K : nullptr, id, L, uniform);
 
     // the rendezvous with the row's merging workgroup
     uint64_t *w = a.lpa_w + (int64_t)slot * (kTicketStride / 2);

@@ -183,11 +183,12 @@ def test_bad_renormalising_logprob_request_is_refused():
     assert "row 3" in last_error(), last_error()
 
 
-def test_renormalising_lists_beyond_the_fused_path_need_small_vocabularies():
-    """Lists longer than 2,048 ids, or lists on rows that also restrict their
-    candidates, take the allowed-id logprob kernels, whose vocabulary bitmap
-    needs V <= 2^19: refused before anything is enqueued.  Short lists have
-    no such limit (they pass validation and fail on the bad row)."""
+def test_long_renormalising_lists_need_small_vocabularies():
+    """Lists longer than 2,048 ids take the bitmap kernels, whose vocabulary
+    bitmap needs V <= 2^19: refused before anything is enqueued.  Shorter
+    lists have no such limit, in the sampling launch or after it (rows that
+    also carry a mask): they pass validation and the call fails on the bad
+    row."""
     V = 2 ** 20
     rows = [dict(SAMPLED), dict(SAMPLED, top_k=0)]
     long_off = (ctypes.c_int64 * 3)(0, 2049, 2049)
@@ -199,7 +200,17 @@ def test_renormalising_lists_beyond_the_fused_path_need_small_vocabularies():
     mask_off = (ctypes.c_int64 * 3)(0, 1, 1)
     ex = extras(allowed=4096, allowed_off=ctypes.cast(mask_off, ctypes.c_void_p))
     assert sample(rows, V=V, lp=lp_allowed_request(short_off), ex=ex) == R.RTS_EINVAL
+    assert "row 1" in last_error(), last_error()
+    assert sample(rows, V=V, lp=lp_allowed_request(long_off), ex=ex) == R.RTS_EINVAL
     assert "2^19" in last_error(), last_error()
+
+
+def test_standalone_long_lists_need_small_vocabularies():
+    V = 2 ** 20
+    off = (ctypes.c_int64 * 2)(0, 2049)
+    rc = R.lib().rts_token_logprobs(FAKE, 1, V, V, FAKE, 5, FAKE, ctypes.cast(off, ctypes.c_void_p),
+                                    FAKE, FAKE, FAKE, FAKE, BIG_WS, None)
+    assert rc == R.RTS_EINVAL and "2^19" in last_error(), last_error()
 
 
 def extras(**kw):
@@ -294,7 +305,9 @@ def test_logprob_argument_checks():
     assert logprobs(allowed=FAKE, off=None) == R.RTS_EINVAL
     assert logprobs(allowed=FAKE, off=[0, 5, 3]) == R.RTS_EINVAL and "decreases" in last_error()
     assert logprobs(allowed=FAKE, off=[-1, 5, 6]) == R.RTS_EINVAL
-    assert logprobs(V=(1 << 19) + 1, allowed=FAKE, off=[0, 5, 6]) == R.RTS_EINVAL
+    # lists longer than 2,048 ids need the vocabulary bitmap (V <= 2^19)
+    assert logprobs(V=(1 << 19) + 1, allowed=FAKE, off=[0, 2049, 2050]) == R.RTS_EINVAL
+    assert "2^19" in last_error()
     assert logprobs(ws_bytes=100) == R.RTS_ENOSPC
     assert logprobs(B=0) == R.RTS_OK
 

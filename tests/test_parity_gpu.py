@@ -412,6 +412,20 @@ def test_allowed_logprobs_are_deterministic_with_duplicates():
     compare_logprobs(first, O.token_logprobs(x, tokens, 20, lists), "allowed dup")
 
 
+def test_allowed_logprobs_past_the_bitmap_vocabulary_limit():
+    """Lists of up to 2,048 ids take the hash-set kernel, which needs no
+    vocabulary bitmap: V = 1,100,003 here (longer lists need V <= 2^19)."""
+    rng = np.random.default_rng(14)
+    Vx = 1_100_003
+    x = rng.normal(0, 3, (3, Vx)).astype(np.float32)
+    lists = [rng.choice(Vx, 2048, replace=False).astype(np.int32),
+             np.concatenate([[7, 7, -1, Vx], rng.integers(0, Vx, 500)]).astype(np.int32), None]
+    tokens = np.array([int(lists[0][5]), 7, 123], np.int32)
+    say("case allowed logprobs V past 2^19")
+    compare_logprobs(gpu_logprobs(x, tokens, 20, lists), O.token_logprobs(x, tokens, 20, lists),
+                     "allowed V past 2^19")
+
+
 def _mixed_params(n, seed):
     rng = np.random.default_rng(seed)
     out = []

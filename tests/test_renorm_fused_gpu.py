@@ -138,7 +138,8 @@ def test_longest_fused_list_and_the_first_longer_one(n):
 
 def test_vocabulary_past_the_standalone_limit():
     """Lists renormalised inside the sampling call need no vocabulary bitmap,
-    so V may exceed 2^19 (the stand-alone kernels' limit)."""
+    so V may exceed 2^19 (the limit of the bitmap kernels that longer lists
+    take)."""
     rng = np.random.default_rng(41)
     Vx = 1_100_003
     x = rng.normal(0, 3, (2, Vx)).astype(np.float32)
