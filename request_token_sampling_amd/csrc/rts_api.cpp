@@ -158,30 +158,35 @@ int check_offsets(int64_t B, const int64_t *off, const char *what)
     return RTS_OK;
 }
 
-// Allowed lists longer than kRenormMax ids take the bitmap kernels, which keep a
-// vocabulary bitmap in LDS: sets *fast_fits when the gather-once kernel's LDS
-// fits too.
-int check_allowed_lds(int64_t V, bool *fast_fits)
+// The bitmap kernels for allowed lists keep a vocabulary bitmap in LDS: true
+// when it fits (V <= 2^19).  Lists of up to kRenormMax ids also have the
+// hash-set kernel, which needs no bitmap; longer ones need the bitmap.
+bool bitmap_fits(int64_t V)
 {
     const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
     const size_t max_lds = V > (1 << 19) ? 0 : max_lds_per_block();
-    if (bitmap_bytes + rts::kAllowedStaticLds > max_lds)
-        return fail(RTS_EINVAL, "allowed lists of more than %d ids need V <= 2^19 (V = %lld)",
-                    rts::kRenormMax, (long long)V);
-    *fast_fits = bitmap_bytes + rts::kAllowedStaticLds <= max_lds;
-    return RTS_OK;
+    return bitmap_bytes + rts::kAllowedStaticLds <= max_lds;
+}
+
+int refuse_long_lists(int64_t V)
+{
+    return fail(RTS_EINVAL, "allowed lists of more than %d ids need V <= 2^19 (V = %lld)",
+                rts::kRenormMax, (long long)V);
 }
 
 // The launches of rts_token_logprobs once its arguments are checked.  Rows
 // with an empty list take the full-row reducer, unless `restricted_only`
-// leaves them out; lists of up to kRenormMax ids the hash-set kernel; longer
-// ones the bitmap kernels (gather-once up to kAllowedFast ids, else walking).
-// ld = 0 makes every row read row 0.
+// leaves them out.  Restricted rows take the bitmap kernels when the bitmap
+// fits (gather-once up to kAllowedFast ids, else walking the bitmap; measured
+// faster than the hash set on 1,000-id lists), else the hash-set kernel
+// (lists of up to kRenormMax ids, checked by the caller).  ld = 0 makes every
+// row read row 0.
 int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, const int32_t *tokens,
                      int32_t top_n, const int32_t *allowed, const int64_t *allowed_off,
                      float *token_lp, int32_t *top_ids, float *top_lp, void *workspace,
-                     bool restricted_only, bool fast_fits, hipStream_t stream)
+                     bool restricted_only, hipStream_t stream)
 {
+    const bool bitmap = bitmap_fits(V);
     const size_t bitmap_bytes = (size_t)((V + 31) / 32) * 4u;
     bool any_restricted = false;
     if (allowed != nullptr)
@@ -233,10 +238,10 @@ int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, cons
         };
         for (int64_t r = 0; r < B; ++r) {
             const int64_t cnt = allowed ? allowed_off[r + 1] - allowed_off[r] : 0;
-            const int row_kind = cnt == 0                  ? 0
-                                 : cnt <= rts::kRenormMax ? rts::kAllowedHash
-                                 : (fast_fits && cnt <= rts::kAllowedFast) ? rts::kAllowedFastBitmap
-                                                                           : rts::kAllowedWide;
+            const int row_kind = cnt == 0  ? 0
+                                 : !bitmap ? rts::kAllowedHash
+                                 : cnt <= rts::kAllowedFast ? rts::kAllowedFastBitmap
+                                                            : rts::kAllowedWide;
             if (row_kind != kind) continue;
             rts::LogprobRow &lr = a.row[n++];
             lr.row = (int32_t)r;
@@ -368,13 +373,12 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     const int32_t *lpa = lp ? lp->allowed : nullptr;
     const int64_t *lpa_off = lpa ? lp->allowed_off : nullptr;
     int64_t lpa_max = 0;
-    bool lpa_fused = false, lpa_fast = false;
+    bool lpa_fused = false;
     if (lpa != nullptr) {
         for (int64_t r = 0; r < B; ++r)
             if (lpa_off[r + 1] - lpa_off[r] > lpa_max) lpa_max = lpa_off[r + 1] - lpa_off[r];
         lpa_fused = allowed == nullptr && lpa_max <= rts::kRenormMax && lpa_off[B] <= 0x7FFFFFFFLL;
-        if (!lpa_fused && lpa_max > rts::kRenormMax)
-            if (const int e = check_allowed_lds(V, &lpa_fast)) return e;
+        if (!lpa_fused && lpa_max > rts::kRenormMax && !bitmap_fits(V)) return refuse_long_lists(V);
     }
 
     // Check every row before enqueuing anything.
@@ -465,7 +469,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (lpa != nullptr && !lpa_fused && lpa_max > 0)
         return enqueue_logprobs(logits, B, V, ld, token, lp->top_n, lpa, lpa_off,
                                 lp->allowed_token_lp, lp->allowed_top_ids, lp->allowed_top_lp,
-                                workspace, true, lpa_fast, stream);
+                                workspace, true, stream);
     return RTS_OK;
 }
 
@@ -495,18 +499,17 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (ws_bytes < need)
         return fail(RTS_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, need);
 
-    // Restricted rows: lists of up to kRenormMax ids take the hash-set kernel
-    // (any V); longer ones the bitmap kernels, which need V <= 2^19.
-    bool any_long = false, fast_fits = false;
+    // Restricted rows: the bitmap kernels where V <= 2^19, else the hash-set
+    // kernel, which takes lists of up to kRenormMax ids.
     if (allowed != nullptr) {
         if (const int e = check_offsets(B, allowed_off, "allowed_off")) return e;
+        bool any_long = false;
         for (int64_t r = 0; r < B; ++r)
             if (allowed_off[r + 1] - allowed_off[r] > rts::kRenormMax) any_long = true;
-        if (any_long)
-            if (const int e = check_allowed_lds(V, &fast_fits)) return e;
+        if (any_long && !bitmap_fits(V)) return refuse_long_lists(V);
     }
     return enqueue_logprobs(logits, B, V, ld, tokens, top_n, allowed, allowed_off, token_lp, top_ids,
-                            top_lp, workspace, false, fast_fits, stream);
+                            top_lp, workspace, false, stream);
 }
 
 int rts_sample_tokens_prior(int design, const float *logits, int64_t B, int64_t V, int64_t ld,

@@ -13,12 +13,12 @@
 // keys (rts_select.h), and publishes one (max, sum) pair and K keys.  The
 // last workgroup of the row combines the pairs in fp64 in chunk order and
 // merges the keys.
-// Restricted rows: one workgroup per row.  Lists of up to kRenormMax ids
-// drop repeats and foreign ids with a hash set in LDS (rts_renorm.h), for any
-// V.  Longer lists use an LDS bitmap of the vocabulary (V <= 2^19): lists of
-// up to kAllowedFast ids are gathered at once into registers, the thread that
-// sets an id's bit owning it; longer ones are marked first and the set bits
-// walked, so each member is gathered exactly once.
+// Restricted rows: one workgroup per row.  Where an LDS bitmap of the
+// vocabulary fits (V <= 2^19) it drops repeats and foreign ids: lists of up to
+// kAllowedFast ids are gathered at once into registers, the thread that sets
+// an id's bit owning it; longer ones are marked first and the set bits walked,
+// so each member is gathered exactly once.  Larger vocabularies take a hash
+// set in LDS instead (rts_renorm.h), for lists of up to kRenormMax ids.
 #include "rts_renorm.h"
 
 namespace rts {
