@@ -99,8 +99,8 @@ typedef struct rts_row_params {
  * When no row also has an rts_sample_extras list and every list holds at
  * most 2,048 ids, these are computed by extra workgroups of the sampling
  * launch, overlapped with it.  Otherwise a second launch computes them after
- * the draw, and the lists then need V <= 2^19 as for rts_token_logprobs
- * (RTS_EINVAL before anything is enqueued).
+ * the draw, as rts_token_logprobs does (lists longer than 2,048 ids then need
+ * V <= 2^19; RTS_EINVAL before anything is enqueued).
  */
 typedef struct rts_logprob_request {
     int32_t top_n;
@@ -226,7 +226,9 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
  *   allowed     device int32 ids, row r owning allowed[allowed_off[r] ..
  *               allowed_off[r+1]); NULL for no restriction.  A row with an
  *               empty range is unrestricted; duplicates count once; ids
- *               outside [0, V) are ignored.  Restricted rows need V <= 2^19.
+ *               outside [0, V) are ignored.  Lists longer than 2,048 ids need
+ *               V <= 2^19 (a vocabulary bitmap in LDS); shorter ones take a
+ *               hash set past that size.
  *   allowed_off host int64 [B+1], non-decreasing, allowed_off[0] >= 0.
  * Outputs (device): token_lp f32 [B] (-inf when the token is outside the
  * row's domain), top_ids int32 [B][top_n] and top_lp f32 [B][top_n], the
