@@ -218,7 +218,15 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Log-softmax of the raw logits (before penalties and temperature), per row.
+ * Log-softmax of the raw logits (before penalties and temperature), per row:
+ * the OpenAI logprobs and top_logprobs of page "#3200 [Engine] OpenAI
+ * logprobs / top_logprobs / allowed_token_ids for the CUDA/HIP engine"
+ * ("Problem and result": up to 20 alternatives per token, and with
+ * allowed_token_ids a distribution renormalised over exactly the listed ids;
+ * "Approach": the values are the model's own distribution, taken from the
+ * head logits before the sampling chain), which page "#1916 OpenAI logprobs
+ * on /v1/chat/completions for the CUDA/HIP engine" ("What changed") takes
+ * from the same head logits as the sampled token.
  *   logits      device fp32 [B][ld] as above; NaN counts as -inf, +inf as
  *               the largest finite float.
  *   tokens      device int32 [B]: the ids whose logprob is reported.
@@ -240,49 +248,6 @@ int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,
                        const int32_t *allowed, const int64_t *allowed_off,
                        float *token_lp, int32_t *top_ids, float *top_lp,
                        void *workspace, size_t ws_bytes, hipStream_t stream);
-
-/*
- * The pages' earlier designs of the same chain, kept as measured ablations of
- * rts_sample_tokens (#19, "What changed", the one-block-per-token and the
- * min_p-and-penalties paragraphs).  Same outputs, bit for bit:
- *   RTS_PRIOR_THREAD   one thread per row: top_k as k sequential
- *                      full-vocabulary scans (the design the pages replaced);
- *   RTS_PRIOR_BLOCK    one workgroup per row: k argmax rounds, each a wave
- *                      then workgroup reduction over the whole row; penalty
- *                      counts through a per-row token bitmap in LDS, a
- *                      flagged id scanning the window;
- *   RTS_PRIOR_RECOUNT  the same with every id scanning the window (the naive
- *                      O(k * V * window) recount the bitmap replaced).
- * Arguments as in rts_sample_tokens (host counters only, no logprobs, no
- * extras); V <= 2^20.  The kernels reread the row k times: they exist to be
- * measured against the single-pass kernel, not to be used.
- */
-#define RTS_PRIOR_THREAD 1
-#define RTS_PRIOR_BLOCK 2
-#define RTS_PRIOR_RECOUNT 3
-int rts_sample_tokens_prior(int design, const float *logits, int64_t B, int64_t V, int64_t ld,
-                            const rts_row_params *params,
-                            const int32_t *history, int64_t H, int64_t ldh,
-                            const int32_t *history_len,
-                            int32_t *token, int32_t *counts, int32_t *kept_ids,
-                            float *kept_logits, uint32_t *philox_x0,
-                            void *workspace, size_t ws_bytes, hipStream_t stream);
-
-/*
- * A plain streaming read of the rows, the measuring stick for the sampler's
- * bandwidth: the same grid, chunking, 16-byte loads and row-major layout as
- * rts_sample_tokens over the same B rows, with only a maximum taken per
- * chunk and no selection, merge or draw.  Its duration is the practical
- * floor of any one-pass kernel over those bytes.
- *   logits     device fp32 [B][ld] as in rts_sample_tokens.
- *   chunk_max  device fp32 [B][ceil(V / 1024)]; row r's first C entries
- *              receive its chunk maxima (C = the sampler's chunk count for
- *              this B and V), NaN ignored.
- * Errors: RTS_EINVAL for bad shapes or NULL pointers; RTS_EDEVICE if the
- * launch fails.  B = 0 is a no-op.
- */
-int rts_read_rows(const float *logits, int64_t B, int64_t V, int64_t ld, float *chunk_max,
-                  hipStream_t stream);
 
 /* Static description of an error code. */
 const char *rts_strerror(int code);

@@ -126,6 +126,31 @@ int oracle_penalised_row(const float *x, int64_t V, const oracle_row_params *p,
     return 0;
 }
 
+/* Temperature and the inverse CDF at u over the first n kept logits y[0..n)
+ * (R6): weights exp((y_i - y_0) / T) in fp64, cdf_j their normalised running
+ * sum, the pick is the first j with cdf_j > u (cdf_{n-1} = 1).  Bit j of
+ * *edges is set when |cdf_j - u| < 1e-6 for j < n - 1: there another correct
+ * fp64 evaluation may pick j + 1 instead of j or the other way round. */
+int oracle_draw_on_prefix(const float *y, int n, float temperature, double u, uint64_t *edges)
+{
+    *edges = 0;
+    int pick = n - 1;
+    if (n > 1) {
+        const double y0 = (double)y[0];
+        const double T = (double)temperature;
+        double z = 0.0;
+        for (int i = 0; i < n; ++i) z += exp(((double)y[i] - y0) / T);
+        double run = 0.0;
+        for (int j = 0; j < n - 1; ++j) {
+            run += exp(((double)y[j] - y0) / T);
+            const double cj = run / z;
+            if (fabs(cj - u) < 1e-6) *edges |= 1ull << j;
+            if (cj > u) { pick = j; break; }
+        }
+    }
+    return pick;
+}
+
 /* The chain after the penalties, over a domain of nd candidates already in
  * the selection order (s sorted by logit desc, index asc). */
 static void chain_on_sorted(const scored *s, int64_t nd, const oracle_row_params *p,
@@ -192,20 +217,11 @@ static void chain_on_sorted(const scored *s, int64_t nd, const oracle_row_params
     }
 
     /* temperature, then the inverse CDF at u (R6). */
-    const double ud = *u;
-    int pick = n - 1;                                   /* cdf_{n-1} = 1 > u */
-    if (n > 1) {
-        const double T = (double)p->temperature;
-        double z = 0.0;
-        for (int i = 0; i < n; ++i) z += exp(((double)s[i].y - y0) / T);
-        double run = 0.0;
-        for (int j = 0; j < n - 1; ++j) {
-            run += exp(((double)s[j].y - y0) / T);
-            const double cj = run / z;
-            if (fabs(cj - ud) < 1e-6) *flags |= ORACLE_FLAG_DRAW_EDGE;
-            if (cj > ud) { pick = j; break; }
-        }
-    }
+    float yk[64];
+    for (int i = 0; i < n; ++i) yk[i] = s[i].y;
+    uint64_t edges = 0;
+    const int pick = oracle_draw_on_prefix(yk, n, p->temperature, *u, &edges);
+    if (edges) *flags |= ORACLE_FLAG_DRAW_EDGE;
     *token = s[pick].i;
     counts[0] = k_eff;
     counts[1] = m;

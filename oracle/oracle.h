@@ -76,6 +76,13 @@ int oracle_sample_row_masked(const float *x, int64_t V, const oracle_row_params 
 int oracle_accept_windows(const int32_t *token, int64_t B, int32_t window,
                           const int32_t *draft, int32_t *accepted);
 
+/* The draw alone (temperature, then the inverse CDF at u) over the first n
+ * kept logits y[0..n), n in 1..64; returns the picked position.  Bit j of
+ * *edges marks |cdf_j - u| < 1e-6 (a flagged draw, where another correct
+ * fp64 evaluation may pick position j + 1 instead of j, or j instead of
+ * j + 1). */
+int oracle_draw_on_prefix(const float *y, int n, float temperature, double u, uint64_t *edges);
+
 /* Penalised and sanitised logits of one row (the chain's first two steps). */
 int oracle_penalised_row(const float *x, int64_t V, const oracle_row_params *p,
                          const int32_t *hist, int64_t hlen, float *y);

@@ -71,7 +71,8 @@ def lib():
         L.oracle_sample_row_masked.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
                                                P, ctypes.c_int64, P, P, P, P, P, P, P]
         L.oracle_accept_windows.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
-        for f in ("oracle_sample_row", "oracle_penalised_row", "oracle_sample_tokens",
+        L.oracle_draw_on_prefix.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_double, P]
+        for f in ("oracle_draw_on_prefix", "oracle_sample_row", "oracle_penalised_row", "oracle_sample_tokens",
                   "oracle_token_logprobs_row", "oracle_sample_row_masked",
                   "oracle_accept_windows"):
             getattr(L, f).restype = ctypes.c_int
@@ -108,6 +109,20 @@ def philox4x32_10(ctr, key):
     return out
 
 
+def draw_on_prefix(kept_logits, temperature: float, u: float):
+    """The draw alone over the kept logits given (temperature, then the
+    inverse CDF at u): (picked position, positions j whose CDF value lies
+    within 1e-6 of u)."""
+    y = np.ascontiguousarray(kept_logits, dtype=np.float32)
+    if not 1 <= y.size <= 64:
+        raise ValueError("draw_on_prefix takes 1..64 logits")
+    edges = np.zeros(1, np.uint64)
+    pick = lib().oracle_draw_on_prefix(_ptr(y), int(y.size), float(temperature), float(u),
+                                       _ptr(edges))
+    e = int(edges[0])
+    return int(pick), [j for j in range(64) if (e >> j) & 1]
+
+
 def penalised_row(x, params: dict, hist=None):
     x = np.ascontiguousarray(x, dtype=np.float32)
     h = None if hist is None else np.ascontiguousarray(hist, dtype=np.int32)
@@ -141,7 +156,8 @@ def sample_row(x, params: dict, hist=None, allowed=None) -> dict:
     if rc != 0:
         raise ValueError("oracle_sample_row refused its input")
     return dict(token=int(tok[0]), counts=counts, kept_ids=kid, kept_logits=klg,
-                x0=int(x0[0]), u=float(u[0]), flags=int(fl[0]))
+                x0=int(x0[0]), u=float(u[0]), flags=int(fl[0]),
+                temperature=float(p.temperature))
 
 
 def sample_tokens(logits, params: list, history=None, hist_len=None) -> dict:
@@ -168,7 +184,7 @@ def sample_tokens(logits, params: list, history=None, hist_len=None) -> dict:
     if rc != 0:
         raise ValueError("oracle_sample_tokens refused its input")
     return dict(token=tok, counts=counts, kept_ids=kid, kept_logits=klg, x0=x0, u=u,
-                flags=fl)
+                flags=fl, temperature=np.array([a.temperature for a in arr[:B]], np.float32))
 
 
 def token_logprobs_row(x, token: int, top_n: int, allowed=None) -> dict:
@@ -220,7 +236,8 @@ def sample_tokens_masked(logits, params: list, allowed_lists, history=None,
                 kept_logits=np.stack([o["kept_logits"] for o in outs]),
                 x0=np.array([o["x0"] for o in outs], np.uint32),
                 u=np.array([o["u"] for o in outs], np.float64),
-                flags=np.array([o["flags"] for o in outs], np.int32))
+                flags=np.array([o["flags"] for o in outs], np.int32),
+                temperature=np.array([o["temperature"] for o in outs], np.float32))
 
 
 def accept_windows(tokens, window: int, drafts) -> np.ndarray:

@@ -1,4 +1,4 @@
-// rts_api.cpp -- the C ABI declared in include/rts.h: argument checks, the
+// rts_api.cpp -- the C ABI declared in include/rts.h and include/rts_measure.h: argument checks, the
 // per-launch argument blocks, chunk sizing and the launches.  Every check
 // runs before anything is enqueued, so a refused call writes nothing (page
 // "#19 serve: per-request temperature/top_p/top_k/min_p/penalties sampling",
@@ -6,6 +6,7 @@
 // than left to write a stale token, and a bad sampling value is refused
 // rather than silently changed).
 #include "rts.h"
+#include "rts_measure.h"
 
 #include <cmath>
 #include <cstdarg>

@@ -476,3 +476,127 @@ def test_logprobs_degenerate_rows(oracle_mod):
     assert list(o["top_ids"]) == [0, 1, 2]
     o = oracle_mod.token_logprobs_row(np.zeros(10, np.float32), 4, 2, np.array([11, -3], np.int32))
     assert o["token_lp"] == -np.inf and list(o["top_ids"]) == [-1, -1]
+
+
+# --------------------------------------------------------------------------
+# Batch dispatch: which history row and which length each row reads.
+# Page #19, "What changed", the min_p and penalties paragraph: the serve loop
+# uploads one history row per verify window and the window's rows share it;
+# a row without one takes the neutral path.  The batch calls are checked row
+# by row against the single-row chain given the window sliced out by hand
+# (the last min(penalty_last_n, len) ids of the named row), so a slip in the
+# row or length a batch row reads fails here, on the CPU.
+# --------------------------------------------------------------------------
+DISPATCH_V = 2048
+DISPATCH_HEAD = 256  # the history ids live here, in the head of every row
+
+
+def dispatch_case():
+    rng = np.random.default_rng(2024)
+    B, V = 9, DISPATCH_V
+    x = rng.normal(0.0, 1.0, (B, V)).astype(np.float32)
+    x[:, :DISPATCH_HEAD] += np.float32(6.0)
+    H, ldh = 3, 320
+    hist_len = np.array([300, 150, 0], np.int32)
+    # every slot of every row holds a head id, so reading past a row's length
+    # or another row changes the counts; a few foreign ids are mixed in
+    history = rng.integers(0, DISPATCH_HEAD, (H, ldh)).astype(np.int32)
+    history[0, 290:296] = [-3, V, V + 7, -1, 5, 5]
+    history[1, 140:143] = [V + 1, -100, 7]
+    # out of order, shared rows, a row with none; windows -1 (all), 0 (off),
+    # 8 and 500 (clamped to the row's length)
+    hrow = [2, 0, 1, -1, 1, 0, 2, 0, 1]
+    last_n = [-1, 8, 500, -1, 0, -1, 8, 500, 8]
+    params = [W.row_params(temperature=0.9, top_k=64, top_p=0.95, min_p=0.02,
+                           penalty_repeat=1.7, penalty_freq=0.9, penalty_present=0.6,
+                           penalty_last_n=last_n[r], history_row=hrow[r], seed=100 + r,
+                           counter=r) for r in range(B)]
+    return x, history, hist_len, params
+
+
+def hand_window(history, hist_len, p):
+    """The row's penalty window sliced by hand: the last
+    min(penalty_last_n, len) ids of its history row (all for -1, none for 0)."""
+    h = p["history_row"]
+    if h < 0:
+        return np.zeros(0, np.int32)
+    n = int(hist_len[h])
+    k = n if p["penalty_last_n"] < 0 else min(p["penalty_last_n"], n)
+    return np.asarray(history[h][n - k:n], np.int32)
+
+
+def single_row_on_window(oracle_mod, x_row, p, win, allowed=None):
+    """The single-row chain given exactly `win` as the whole window."""
+    if win.size == 0:
+        return oracle_mod.sample_row(x_row, dict(p, history_row=-1), None, allowed)
+    return oracle_mod.sample_row(x_row, dict(p, history_row=0, penalty_last_n=-1), win, allowed)
+
+
+def assert_rows_equal(batch, r, one, tag):
+    for key in ("counts", "kept_ids", "kept_logits"):
+        assert np.array_equal(batch[key][r], one[key]), (tag, r, key)
+    for key in ("token", "x0", "flags"):
+        assert int(batch[key][r]) == int(one[key]), (tag, r, key)
+
+
+def test_batch_dispatch_reads_the_named_history_row(oracle_mod):
+    x, history, hist_len, params = dispatch_case()
+    got = oracle_mod.sample_tokens(x, params, history, hist_len)
+    for r, p in enumerate(params):
+        win = hand_window(history, hist_len, p)
+        one = single_row_on_window(oracle_mod, x[r], p, win)
+        assert_rows_equal(got, r, one, "sample_tokens")
+        # the fixture sees its feature: a row with a non-empty window is
+        # penalised, and the penalties change its kept logits
+        plain = oracle_mod.sample_row(x[r], dict(p, history_row=-1))
+        assert (win.size > 0) == (not np.array_equal(one["kept_logits"], plain["kept_logits"])), r
+    # the windows differ between the rows that share a history row, so the
+    # length slicing is visible: rows 1 and 7 both name row 0 (8 vs 300 ids)
+    assert hand_window(history, hist_len, params[1]).size == 8
+    assert hand_window(history, hist_len, params[7]).size == 300
+    assert not np.array_equal(got["kept_ids"][1], single_row_on_window(
+        oracle_mod, x[1], params[1], hand_window(history, hist_len, params[7]))["kept_ids"])
+
+
+def test_masked_batch_dispatch_reads_the_named_history_row(oracle_mod):
+    x, history, hist_len, params = dispatch_case()
+    rng = np.random.default_rng(77)
+    lists = [None, rng.choice(DISPATCH_HEAD, 90, replace=False).astype(np.int32),
+             np.zeros(0, np.int32), rng.choice(DISPATCH_V, 300, replace=False).astype(np.int32),
+             None, np.array([3, 3, 9, -1, DISPATCH_V, 200], np.int32),
+             rng.choice(DISPATCH_HEAD, 40, replace=False).astype(np.int32), None,
+             np.arange(0, 120, dtype=np.int32)]
+    got = oracle_mod.sample_tokens_masked(x, params, lists, history, hist_len)
+    for r, p in enumerate(params):
+        win = hand_window(history, hist_len, p)
+        one = single_row_on_window(oracle_mod, x[r], p, win, lists[r])
+        assert_rows_equal(got, r, one, "sample_tokens_masked")
+        if lists[r] is not None and lists[r].size:
+            members = set(int(i) for i in lists[r] if 0 <= i < DISPATCH_V)
+            k = int(one["counts"][0])
+            assert set(one["kept_ids"][:k].tolist()) <= members, r
+
+
+def test_draw_on_prefix_is_the_chain_draw(oracle_mod):
+    """The draw alone (used to judge flagged rows) is the chain's own draw:
+    over the chain's kept prefix it returns the chain's pick, it matches the
+    inverse CDF of scipy's tempered softmax, and it marks an edge exactly on
+    the rows the chain flags for the draw."""
+    rng = np.random.default_rng(43)
+    x = rng.normal(0, 1.5, 400).astype(np.float32)
+    for c in range(300):
+        T = float(np.float32(rng.uniform(0.2, 2.0)))
+        o = oracle_mod.sample_row(x, sampled(top_k=16, top_p=0.9, temperature=T, seed=3,
+                                             counter=c))
+        n = int(o["counts"][2])
+        pick, edges = oracle_mod.draw_on_prefix(o["kept_logits"][:n], T, o["u"])
+        assert o["kept_ids"][pick] == o["token"], c
+        assert bool(edges) == bool(o["flags"] & oracle_mod.FLAG_DRAW_EDGE), c
+        cdf = np.cumsum(scipy.special.softmax(o["kept_logits"][:n].astype(np.float64) / T))
+        if np.min(np.abs(cdf - o["u"])) > 1e-9:
+            assert pick == min(int(np.searchsorted(cdf, o["u"], side="right")), n - 1), c
+    # a hand case with a step exactly at u: weights 1 and 1 (cdf_0 = 0.5)
+    pick, edges = oracle_mod.draw_on_prefix(np.array([1.0, 1.0], np.float32), 1.0, 0.5)
+    assert pick == 1 and edges == [0]
+    pick, edges = oracle_mod.draw_on_prefix(np.array([1.0, 1.0], np.float32), 1.0, 0.4999)
+    assert pick == 0 and edges == []
