@@ -218,6 +218,35 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                       void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rts_sample_tokens for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, outputs, errors and results are those of
+ * rts_sample_tokens without `workspace` / `ws_bytes`: the scratch memory
+ * comes from one static device array inside the library,
+ * rts_noalloc_scratch_bytes() bytes (16 MiB) per GPU, held by every GPU the
+ * library runs on until the process ends.  The call allocates nothing.
+ *  - Calls whose rows need more scratch than that (rts_workspace_bytes(B, V)
+ *    above it; 64 rows fit V <= 394,240) return RTS_ENOSPC before anything
+ *    is enqueued, with rts_last_error() giving both sizes.
+ *  - The first call on a device looks the array up for that device and
+ *    enqueues one small kernel on `stream` that zeroes its counters; every
+ *    call leaves them zeroed for the next.
+ *  - Every call on one GPU shares that GPU's array: calls that can overlap on
+ *    one GPU (two streams, two host threads) race and must be serialised by
+ *    the caller.
+ */
+size_t rts_noalloc_scratch_bytes(void);
+int rts_sample_tokens_noalloc(const float *logits, int64_t B, int64_t V, int64_t ld,
+                              const rts_row_params *params,
+                              const int32_t *history, int64_t H, int64_t ldh,
+                              const int32_t *history_len,
+                              int32_t *token, int32_t *counts, int32_t *kept_ids,
+                              float *kept_logits, uint32_t *philox_x0,
+                              uint64_t *counters, int64_t counter_stride,
+                              const rts_logprob_request *lp, const rts_sample_extras *ex,
+                              hipStream_t stream);
+
+/*
  * Log-softmax of the raw logits (before penalties and temperature), per row:
  * the OpenAI logprobs and top_logprobs of page "#3200 [Engine] OpenAI
  * logprobs / top_logprobs / allowed_token_ids for the CUDA/HIP engine"

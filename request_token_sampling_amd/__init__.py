@@ -113,8 +113,13 @@ def lib() -> ctypes.CDLL:
         L.rts_read_rows.argtypes = [P, I64, I64, I64, P, P]
         L.rts_sample_tokens_prior.argtypes = [I32, P, I64, I64, I64, P, P, I64, I64, P, P, P, P,
                                               P, P, P, SZ, P]
+        L.rts_sample_tokens_noalloc.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, P, P,
+                                                P, P, I64, P, P, P]
+        L.rts_noalloc_scratch_bytes.argtypes = []
+        L.rts_noalloc_scratch_bytes.restype = ctypes.c_size_t
         for f in ("rts_workspace_bytes", "rts_workspace_init", "rts_sample_tokens",
-                  "rts_token_logprobs", "rts_read_rows", "rts_sample_tokens_prior"):
+                  "rts_token_logprobs", "rts_read_rows", "rts_sample_tokens_prior",
+                  "rts_sample_tokens_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.rts_strerror.argtypes = [ctypes.c_int]
         L.rts_strerror.restype = ctypes.c_char_p
@@ -181,15 +186,20 @@ class SampleCall:
     def __init__(self, logits, params, history=None, history_len=None, workspace=None,
                  stream=None, counters=None, counter_stride=0, logprobs=None, window=0,
                  draft=None, allowed=None, allowed_off=None, ignored=None,
-                 logprob_allowed=None, logprob_allowed_off=None):
+                 logprob_allowed=None, logprob_allowed_off=None, noalloc=False):
         self.logits, self.B, self.V, self.ld = _rows_view(logits)
         dev = self.logits.device
+        # noalloc: call rts_sample_tokens_noalloc (the library's static scratch)
+        self.noalloc = bool(noalloc)
+        if self.noalloc and workspace is not None:
+            raise ValueError("noalloc calls take no workspace")
         self.token = torch.empty(self.B, dtype=torch.int32, device=dev)
         self.counts = torch.empty((self.B, 3), dtype=torch.int32, device=dev)
         self.kept_ids = torch.empty((self.B, KEPT), dtype=torch.int32, device=dev)
         self.kept_logits = torch.empty((self.B, KEPT), dtype=torch.float32, device=dev)
         self.philox_x0 = torch.empty(self.B, dtype=torch.int32, device=dev)
-        self.workspace = workspace if workspace is not None else make_workspace(self.B, self.V, dev)
+        self.workspace = (None if self.noalloc else
+                          workspace if workspace is not None else make_workspace(self.B, self.V, dev))
         self.history = history
         if history is not None:
             if history.dtype != torch.int32 or history.dim() != 2 or history.stride(1) != 1:
@@ -268,7 +278,7 @@ class SampleCall:
             _ptr(self.philox_x0), _ptr(self.counters), self.counter_stride,
             None if self.lp is None else ctypes.byref(self.lp),
             None if self.ex is None else ctypes.byref(self.ex),
-            _ptr(self.workspace), self.workspace.numel(), None]
+            _ptr(self.workspace), 0 if self.workspace is None else self.workspace.numel(), None]
 
     def __call__(self):
         if self._args is None:
@@ -276,7 +286,11 @@ class SampleCall:
         a = self._args
         a[0] = self.logits.data_ptr()
         a[20] = _stream_handle(self.stream)
-        _check(lib().rts_sample_tokens(*a))
+        if self.noalloc:
+            # rts_sample_tokens_noalloc: the same arguments without the workspace
+            _check(lib().rts_sample_tokens_noalloc(*a[:18], a[20]))
+        else:
+            _check(lib().rts_sample_tokens(*a))
         return self
 
     def results(self) -> dict:
@@ -321,6 +335,21 @@ def sample_tokens(logits, params, history=None, history_len=None, workspace=None
     return SampleCall(logits, params, history, history_len, workspace, stream, counters,
                       counter_stride, logprobs, window, draft, allowed, allowed_off,
                       ignored, logprob_allowed, logprob_allowed_off)().results()
+
+
+def sample_tokens_noalloc(logits, params, history=None, history_len=None, stream=None,
+                          counters=None, counter_stride=0, logprobs=None, window=0, draft=None,
+                          allowed=None, allowed_off=None, ignored=None, logprob_allowed=None,
+                          logprob_allowed_off=None) -> dict:
+    """sample_tokens through rts_sample_tokens_noalloc: no workspace, the
+    library's static scratch instead (see include/rts.h)."""
+    return SampleCall(logits, params, history, history_len, None, stream, counters,
+                      counter_stride, logprobs, window, draft, allowed, allowed_off, ignored,
+                      logprob_allowed, logprob_allowed_off, noalloc=True)().results()
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().rts_noalloc_scratch_bytes())
 
 
 class LogprobCall:
@@ -408,7 +437,7 @@ class ReadCall:
         return self
 
 
-__all__ = ["sample_tokens", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
+__all__ = ["sample_tokens", "sample_tokens_noalloc", "noalloc_scratch_bytes", "token_logprobs", "SampleCall", "LogprobCall", "workspace_bytes",
            "make_workspace", "row_params", "RowParams", "LogprobRequest", "SampleExtras", "ReadCall",
            "PriorCall",
            "RTSError",

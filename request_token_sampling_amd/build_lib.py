@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librts.so")
-SOURCES = ["rts_api.cpp", "rts_sample.hip", "rts_logprobs.hip", "rts_prior.hip"]
+SOURCES = ["rts_api.cpp", "rts_sample.hip", "rts_logprobs.hip", "rts_prior.hip",
+           "rts_noalloc.hip"]
 ARCH = os.environ.get("RTS_OFFLOAD_ARCH", "gfx950")
 
 

@@ -263,54 +263,33 @@ int enqueue_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld, cons
 
 }  // namespace
 
-extern "C" {
+namespace rts {
 
-const char *rts_strerror(int code)
+int set_error(int code, const char *fmt, ...)
 {
-    switch (code) {
-    case RTS_OK: return "ok";
-    case RTS_EINVAL: return "invalid argument";
-    case RTS_ENOSPC: return "workspace too small";
-    case RTS_EDEVICE: return "HIP launch error";
-    default: return "unknown error";
-    }
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
 }
 
-const char *rts_last_error(void) { return g_last_error; }
+void clear_last_error() { clear_error(); }
 
-int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes)
+// rts_sample_tokens once its error state is cleared.  With get_ws, the
+// workspace comes from it, asked only after every argument has been checked
+// (so a refused call touches no device); `workspace` is then ignored.
+int sample_tokens_impl(const float *logits, int64_t B, int64_t V, int64_t ld,
+                       const rts_row_params *params,
+                       const int32_t *history, int64_t H, int64_t ldh,
+                       const int32_t *history_len,
+                       int32_t *token, int32_t *counts, int32_t *kept_ids,
+                       float *kept_logits, uint32_t *philox_x0,
+                       uint64_t *counters, int64_t counter_stride,
+                       const rts_logprob_request *lp, const rts_sample_extras *ex,
+                       void *workspace, size_t ws_bytes, WorkspaceProvider get_ws,
+                       hipStream_t stream)
 {
-    clear_error();
-    if (bytes == nullptr) return fail(RTS_EINVAL, "bytes is NULL");
-    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
-    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
-    const int64_t rows = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
-    *bytes = rts::ws_layout(rows, V).total;
-    return RTS_OK;
-}
-
-int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream)
-{
-    clear_error();
-    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
-    if (ws_bytes < rts::kTicketBytes) return fail(RTS_ENOSPC, "workspace of %zu bytes", ws_bytes);
-    const int e = rts::launch_zero_u32(static_cast<uint32_t *>(workspace),
-                                       rts::kTicketBytes / 4u, stream);
-    if (e != 0) return fail(RTS_EDEVICE, "zero kernel: %s", hipGetErrorString((hipError_t)e));
-    return RTS_OK;
-}
-
-int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
-                      const rts_row_params *params,
-                      const int32_t *history, int64_t H, int64_t ldh,
-                      const int32_t *history_len,
-                      int32_t *token, int32_t *counts, int32_t *kept_ids,
-                      float *kept_logits, uint32_t *philox_x0,
-                      uint64_t *counters, int64_t counter_stride,
-                      const rts_logprob_request *lp, const rts_sample_extras *ex,
-                      void *workspace, size_t ws_bytes, hipStream_t stream)
-{
-    clear_error();
     if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
     if (B == 0) return RTS_OK;
     if (B >= 0x7FFFFFFFLL) return fail(RTS_EINVAL, "B = %lld too large", (long long)B);
@@ -322,7 +301,7 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
     if (logits == nullptr) return fail(RTS_EINVAL, "logits is NULL");
     if (params == nullptr) return fail(RTS_EINVAL, "params is NULL");
     if (token == nullptr) return fail(RTS_EINVAL, "token is NULL");
-    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
+    if (workspace == nullptr && get_ws == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
     if (H < 0 || ldh < 0) return fail(RTS_EINVAL, "H = %lld, ldh = %lld", (long long)H, (long long)ldh);
     if (lp != nullptr) {
         if (lp->top_n < 0 || lp->top_n > RTS_MAX_TOP_N)
@@ -384,6 +363,8 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
 
     // Check every row before enqueuing anything.
     if (const int e = check_rows(B, params, history, H, ldh, history_len)) return e;
+    if (get_ws != nullptr)
+        if (const int e = get_ws(&workspace, stream)) return e;
 
     char *ws = static_cast<char *>(workspace);
     const rts::WsLayout L = rts::ws_layout(B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch, V);
@@ -472,6 +453,61 @@ int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
                                 lp->allowed_token_lp, lp->allowed_top_ids, lp->allowed_top_lp,
                                 workspace, true, stream);
     return RTS_OK;
+}
+
+}  // namespace rts
+
+extern "C" {
+
+const char *rts_strerror(int code)
+{
+    switch (code) {
+    case RTS_OK: return "ok";
+    case RTS_EINVAL: return "invalid argument";
+    case RTS_ENOSPC: return "workspace too small";
+    case RTS_EDEVICE: return "HIP launch error";
+    default: return "unknown error";
+    }
+}
+
+const char *rts_last_error(void) { return g_last_error; }
+
+int rts_workspace_bytes(int64_t B, int64_t V, size_t *bytes)
+{
+    clear_error();
+    if (bytes == nullptr) return fail(RTS_EINVAL, "bytes is NULL");
+    if (B < 0) return fail(RTS_EINVAL, "B = %lld < 0", (long long)B);
+    if (V <= 0 || V > RTS_MAX_V) return fail(RTS_EINVAL, "V = %lld outside 1..2^30", (long long)V);
+    const int64_t rows = B < rts::kRowsPerLaunch ? B : rts::kRowsPerLaunch;
+    *bytes = rts::ws_layout(rows, V).total;
+    return RTS_OK;
+}
+
+int rts_workspace_init(void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (workspace == nullptr) return fail(RTS_EINVAL, "workspace is NULL");
+    if (ws_bytes < rts::kTicketBytes) return fail(RTS_ENOSPC, "workspace of %zu bytes", ws_bytes);
+    const int e = rts::launch_zero_u32(static_cast<uint32_t *>(workspace),
+                                       rts::kTicketBytes / 4u, stream);
+    if (e != 0) return fail(RTS_EDEVICE, "zero kernel: %s", hipGetErrorString((hipError_t)e));
+    return RTS_OK;
+}
+
+int rts_sample_tokens(const float *logits, int64_t B, int64_t V, int64_t ld,
+                      const rts_row_params *params,
+                      const int32_t *history, int64_t H, int64_t ldh,
+                      const int32_t *history_len,
+                      int32_t *token, int32_t *counts, int32_t *kept_ids,
+                      float *kept_logits, uint32_t *philox_x0,
+                      uint64_t *counters, int64_t counter_stride,
+                      const rts_logprob_request *lp, const rts_sample_extras *ex,
+                      void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    return rts::sample_tokens_impl(logits, B, V, ld, params, history, H, ldh, history_len, token,
+                                   counts, kept_ids, kept_logits, philox_x0, counters,
+                                   counter_stride, lp, ex, workspace, ws_bytes, nullptr, stream);
 }
 
 int rts_token_logprobs(const float *logits, int64_t B, int64_t V, int64_t ld,

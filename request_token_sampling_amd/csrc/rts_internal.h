@@ -6,6 +6,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// the C ABI's argument structs (include/rts.h)
+struct rts_row_params;
+struct rts_logprob_request;
+struct rts_sample_extras;
+
 namespace rts {
 
 constexpr int kBlock = 256;          // threads per workgroup: four 64-lane waves
@@ -179,6 +184,25 @@ __host__ __device__ inline int sample_work(int rows, int nchunks, int early, int
     const int P = xcds_used(early);
     return rows * ((nchunks + P - 1) / P) * P;
 }
+
+// A workspace handed out after a call's arguments are checked (the static
+// scratch of rts_sample_tokens_noalloc); returns an RTS_* code.
+typedef int (*WorkspaceProvider)(void **workspace, hipStream_t stream);
+
+// The body of rts_sample_tokens (rts_api.cpp), shared with the allocation-
+// free entry point, and the thread's rts_last_error text.
+int sample_tokens_impl(const float *logits, int64_t B, int64_t V, int64_t ld,
+                       const ::rts_row_params *params,
+                       const int32_t *history, int64_t H, int64_t ldh,
+                       const int32_t *history_len,
+                       int32_t *token, int32_t *counts, int32_t *kept_ids,
+                       float *kept_logits, uint32_t *philox_x0,
+                       uint64_t *counters, int64_t counter_stride,
+                       const ::rts_logprob_request *lp, const ::rts_sample_extras *ex,
+                       void *workspace, size_t ws_bytes, WorkspaceProvider get_ws,
+                       hipStream_t stream);
+int set_error(int code, const char *fmt, ...);
+void clear_last_error();
 
 // Launchers (return a hipError_t as int).
 int launch_sample(const SampleArgs &a, int ept, bool vec, hipStream_t s);
