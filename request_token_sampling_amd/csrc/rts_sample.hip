@@ -36,6 +36,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // The chunk at `base` into registers, element e of the thread at
 // elem_index(base, e); ids past V (only in the last chunk) read as NaN.
+// A chunk wholly below V takes a path with no branch between its loads: a
+// branch whose two sides fill the same registers makes the compiler wait
+// for each 16-byte load before issuing the next (a full vmcnt(0) each).
 // The 16-byte loads carry the nontemporal hint (the `nt` bit): the logits
 // are streamed once, and on MI355X this measured 2-3 % faster on 40 rows and
 // on one row read as two broadcast parameter rows (ld = 0), whose second
@@ -44,6 +47,18 @@ template <int EPT, bool VEC>
 __device__ __forceinline__ void load_chunk(const float *x, int base, int V, float (&v)[EPT])
 {
     const int tid = threadIdx.x;
+    if (VEC && base + (EPT / 4) * 1024 <= V) {
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+            const f32x4 t = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4 *>(x + base + q * 1024 + tid * 4));
+            v[4 * q + 0] = t.x;
+            v[4 * q + 1] = t.y;
+            v[4 * q + 2] = t.z;
+            v[4 * q + 3] = t.w;
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < EPT / 4; ++q) {
         const int i0 = base + q * 1024 + tid * 4;
