@@ -3,6 +3,8 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload single_stream|window|batch|stress]
 python bench.py --summarize-trace KERNEL_STATS_CSV --workload W --cmd "..."
 python bench.py --summarize-pmc FETCH_CSV WRITE_CSV --workload W --cmd "..."
+python bench.py --summarize-counters COUNTER_CSV... --workload W --cmd "..."
+python bench.py --cpu-only     (the oracle's host timing alone)
 
 A step is one pass of the hot path over one batch of the workload:
   single_stream  one row of 248,320 fp32 logits, the sampled chain (top_k 20,
@@ -53,11 +55,15 @@ def parse():
     ap.add_argument("--no-alt", action="store_true",
                     help="skip the separate-launch comparison, so every launch of the sampler "
                          "kernel in the run is the step's own (used for the rocprofv3 averages)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-reps", type=int, default=10,
+                    help="steps per median in the oracle's host timing")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="print only the oracle's host timing (no GPU needed)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (known bytes) for counter scaling")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="COUNTER_CSV")
     ap.add_argument("--cmd", default="", help="profiling command recorded in the summary")
     return ap.parse_args()
 
@@ -312,6 +318,11 @@ def ablations(dev):
         ws = R.make_workspace(wl.B, wl.V, dev)
         single = R.SampleCall(wl.copies[0], params, wl.hist, wl.hist_len, workspace=ws)
         res = {"single_pass_us": per_launch_us(wl, single, 300)}
+        if name == "single_stream":
+            # the greedy pass alone (top_k 1): selection, merge and epilogue
+            # at their shortest, over the same row
+            greedy = R.SampleCall(wl.copies[0], wl.alt_passes[1][1], workspace=ws)
+            res["greedy_only_us"] = per_launch_us(wl, greedy, 300)
         for label, design, n in (("prior_block_us", R.PRIOR_BLOCK, 4 * launches),
                                  ("prior_recount_us", R.PRIOR_RECOUNT, launches),
                                  ("prior_thread_us", R.PRIOR_THREAD, launches)):
@@ -439,6 +450,50 @@ def summarize_trace(path, workload, cmd):
     print(out)
 
 
+# logit bytes one launch of each workload reads (rows x V x 4)
+WORKLOAD_LOGIT_BYTES = {"single_stream": 1 * 248320 * 4, "window": 5 * 248320 * 4,
+                        "batch": 40 * 248320 * 4, "stress": 40 * 248320 * 4}
+
+
+def summarize_counters(paths, workload, cmd):
+    """Median per sampler dispatch of every counter in one or more rocprofv3
+    --pmc counter_collection.csv files (one pass each), with ratios that say
+    where the waves' cycles go."""
+    import statistics
+    vals = {}
+    for path in paths:
+        for r in _csv_rows(path):
+            if "rts::sample_kernel" not in r.get("Kernel_Name", ""):
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in sorted(vals.items())}
+    lines = [f"# rocprofv3 counters of rts::sample_kernel, workload {workload}: median per "
+             f"dispatch over all sampler dispatches",
+             f"# command (one pass per counter group): {cmd}",
+             "# summarised by: python bench.py --summarize-counters "
+             + " ".join(os.path.basename(p) for p in paths) + f" --workload {workload}"]
+    for k, v in med.items():
+        lines.append(f"{k} = {v:.1f}")
+        lines.append(f"{k}_dispatches = {len(vals[k])}")
+
+    def ratio(name, a, b):
+        if a in med and b in med and med[b] > 0:
+            lines.append(f"{name} = {med[a] / med[b]:.4f}")
+    ratio("wait_any_per_wave_cycle", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")
+    ratio("valu_active_per_wave_cycle", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")
+    ratio("salu_per_valu_inst", "SQ_INSTS_SALU", "SQ_INSTS_VALU")
+    ratio("lds_per_valu_inst", "SQ_INSTS_LDS", "SQ_INSTS_VALU")
+    if "SQ_WAVES" in med and med["SQ_WAVES"] > 0:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES"):
+            if k in med:
+                lines.append(f"{k}_per_wave = {med[k] / med['SQ_WAVES']:.1f}")
+    lines.append(f"source_sha256 = {kernel_source_hash()}")
+    out = os.path.join(PROFILES, f"counters_sample_kernel_{workload}.txt")
+    os.makedirs(PROFILES, exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+
+
 def summarize_pmc(fetch_csv, write_csv, workload, cmd):
     """HBM bytes per sampler launch from two rocprofv3 --pmc runs (FETCH_SIZE,
     then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
@@ -449,17 +504,19 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd):
         """Counter values of the sampler dispatches, and of the first three
         copy dispatches of the run: the calibration copies, which run before
         anything else copies on the device."""
-        sample, copies = [], []
+        sample, copies, reads = [], [], []
         for r in _csv_rows(path):
             if r.get("Counter_Name") != counter:
                 continue
             name, val = r["Kernel_Name"], float(r["Counter_Value"])
             if "rts::sample_kernel" in name:
                 sample.append(val)
+            elif "read_rows_kernel" in name:
+                reads.append(val)
             elif "copy" in name.lower():
                 copies.append((int(r["Dispatch_Id"]), val))
         copies.sort()
-        return {"sample": sample, "copy": [v for _, v in copies[:3]]}
+        return {"sample": sample, "copy": [v for _, v in copies[:3]], "read": reads}
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
@@ -483,30 +540,112 @@ def summarize_pmc(fetch_csv, write_csv, workload, cmd):
              f"write_bytes_per_launch = {write_b:.0f}",
              f"hbm_bytes_per_launch = {fetch_b + write_b:.0f}",
              f"source_sha256 = {kernel_source_hash()}"]
+    if f["read"]:
+        # second calibration: rts_read_rows reads every logit of the batch
+        # once with the sampler's own loads, a known byte count per launch
+        known = WORKLOAD_LOGIT_BYTES[workload]
+        r_kib = statistics.median(f["read"])
+        lines += [f"read_rows_dispatches = {len(f['read'])}",
+                  f"read_rows_fetch_kib_raw = {r_kib:.1f}",
+                  f"read_rows_known_bytes = {known}",
+                  f"read_rows_fetch_scale = {known / (r_kib * 1024.0):.4f}",
+                  f"fetch_bytes_per_launch_read_rows_scale = "
+                  f"{f_s * 1024.0 * known / (r_kib * 1024.0):.0f}"]
     out = os.path.join(PROFILES, f"traffic_sample_kernel_{workload}.txt")
     os.makedirs(PROFILES, exist_ok=True)
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
 
 
-def cpu_baseline(seconds):
-    """The oracle as it stands, single-threaded, on the single-stream row
-    (sampled pass plus greedy pass, as one GPU step), for about `seconds`."""
+def host_threads():
+    """Host cores this process may run on (its CPU affinity)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _oracle_step(name):
+    """One workload's step as oracle calls, one job per row: (jobs, rows
+    counted, logit bytes read).  Each job is independent of the others."""
     import oracle.oracle as O
     from request_token_sampling_amd import workloads as W
-    w = W.single_stream()
-    x = w["logits"]
-    O.sample_tokens(x, w["sampled"])
-    n = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        O.sample_tokens(x, w["sampled"])
-        O.sample_tokens(x, w["greedy"])
-        n += 1
-    dt = time.perf_counter() - t0
-    return dict(value=round(n / dt, 3), unit="rows/s", cores=1, kind="oracle",
-                sample=f"{n} single-stream steps (one sampled row of V=248,320 plus its greedy "
-                       f"pass) in {dt:.1f} s on one host thread")
+
+    if name == "single_stream":
+        w = W.single_stream()
+        x = w["logits"][0]
+        jobs = [lambda p=p: O.sample_row(x, p) for p in w["sampled"] + w["greedy"]]
+        return jobs, 1, x.nbytes, "one sampled row of V=248,320 and its greedy pass"
+    if name == "window":
+        vw = W.VerifyWindows()
+        x = vw.next_logits()
+        hist = vw.history.reshape(-1)
+        jobs = [lambda r=r: O.sample_row(x[r], p, hist) for r, p in enumerate(vw.params(0))]
+        return jobs, x.shape[0], x.nbytes, "a verify window of 5 penalised rows"
+    if name == "batch":
+        w = W.batch_slots()
+        x, h, hl = w["logits"], w["history"], w["hist_len"]
+
+        def row(r, p):
+            hr = p.get("history_row", -1)
+            return O.sample_row(x[r], p, None if hr < 0 else h[hr][:int(hl[hr])])
+        jobs = [lambda r=r, p=p: row(r, p) for r, p in enumerate(w["params"])]
+        return jobs, x.shape[0], x.nbytes, "40 penalised batch-slot rows"
+    w = W.logprobs_stress()
+    x, top_n = w["logits"], w["top_n"]
+
+    def row(r, p):
+        t = O.sample_row(x[r], p)["token"]
+        O.token_logprobs_row(x[r], t, top_n)
+        return O.token_logprobs_row(x[r], t, top_n, w["allowed"][r])
+    jobs = [lambda r=r, p=p: row(r, p) for r, p in enumerate(w["params"])]
+    return jobs, x.shape[0], x.nbytes, ("40 rows sampled at top_k 64 with top-20 raw logprobs "
+                                        "and the same over 1,000 allowed ids")
+
+
+def cpu_baseline(reps=10):
+    """The oracle (its C source built -O3 -march=native, same arithmetic as
+    the tests' build) on the host: for each workload, the median of `reps`
+    steps, once on one thread and once with rows spread over every host core
+    (one row per job; the C calls release the GIL).  The one-thread leg of
+    the 40-row workloads times the first 10 rows of the batch (rows/s is per
+    row).  `value` is the single-stream step on every core."""
+    import statistics
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle.oracle as O
+    O.use_native_build()
+    cores = host_threads()
+    out = {}
+    try:
+        for name in ("single_stream", "window", "batch", "stress"):
+            jobs, rows, nbytes, what = _oracle_step(name)
+            res = {"sample": what}
+            for threads in (1, cores):
+                part = jobs[:10] if threads == 1 and len(jobs) > 10 else jobs
+                frac = len(part) / len(jobs)
+                times = []
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    for _ in range(reps):
+                        t0 = time.perf_counter()
+                        list(ex.map(lambda f: f(), part))
+                        times.append(time.perf_counter() - t0)
+                t = statistics.median(times)
+                res[f"threads_{threads}"] = dict(
+                    threads=min(threads, len(part)), cores=cores, reps=reps,
+                    jobs_per_rep=len(part), median_s=round(t, 5),
+                    rows_s=round(rows * frac / t, 3), gb_s=round(nbytes * frac / t / 1e9, 4))
+                progress(f"oracle {name}: {threads} thread(s) {t * 1e3:.1f} ms per rep")
+            out[name] = res
+    finally:
+        O.use_native_build(False)
+    top = out["single_stream"][f"threads_{cores}"]
+    return dict(value=top["rows_s"], unit="rows/s", cores=top["threads"], kind="oracle",
+                host_cores=cores, build="gcc -O3 -march=native -ffp-contract=off",
+                sample=(f"median of {reps} single-stream steps (one sampled row of V=248,320 "
+                        f"and its greedy pass, one job each) over {top['threads']} host "
+                        f"threads; every workload at 1 thread and at {cores} in by_workload"),
+                by_workload=out)
 
 
 def progress(msg):
@@ -520,6 +659,12 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.cmd)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.cmd)
+        return
+    if args.cpu_only:
+        print(json.dumps(cpu_baseline(args.cpu_reps)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the sampler's rows are independent, so a batch "
@@ -575,7 +720,7 @@ def main():
             if name == args.workload:
                 continue
             w2 = Workload(name, dev)
-            steps = max(50, args.steps // 4)
+            steps = max(300, args.steps // 4)
             m2 = measure(w2, steps, max(10, args.warmup // 4), warm=not args.no_warm,
                          alt=not args.no_alt)
             progress(f"{name}: graph {m2['graph_wall'] / steps * 1e3:.4f} ms/step, kernels "
@@ -598,8 +743,8 @@ def main():
     if not args.no_extra:
         line["ablations"] = ablations(dev)
     if not args.no_cpu_baseline:
-        progress(f"oracle on the host for about {args.cpu_seconds} s")
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        progress("oracle on the host: every workload, 1 thread and all host cores")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_reps)
     print(json.dumps(line), flush=True)
 
 

@@ -15,6 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+LIB_NATIVE = os.path.join(HERE, "liboracle_native.so")
 
 FLAG_TOP_P_EDGE = 1
 FLAG_DRAW_EDGE = 2
@@ -37,47 +38,69 @@ class RowParams(ctypes.Structure):
     ]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so next to it."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        tmp = LIB + ".tmp"
+def build(force: bool = True, native: bool = False) -> str:
+    """Compile oracle.c into liboracle.so next to it.  With `native`, the same
+    source with -O3 -march=native into liboracle_native.so: the host-speed
+    build the benchmark times (still -ffp-contract=off and no fast-math, so
+    every result is the one the -O2 build gives)."""
+    out = LIB_NATIVE if native else LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(SRC):
+        tmp = out + ".tmp"
+        opt = ["-O3", "-march=native"] if native else ["-O2"]
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+            ["gcc", *opt, "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-o", tmp, SRC, "-lm"])
-        os.replace(tmp, LIB)
-    return LIB
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
+_lib_native = None
+
+
+def _bind(L):
+    P = ctypes.c_void_p
+    L.oracle_philox4x32_10.argtypes = [P, P, P]
+    L.oracle_philox4x32_10.restype = None
+    L.oracle_sample_row.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
+                                    P, P, P, P, P, P, P]
+    L.oracle_penalised_row.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64, P]
+    L.oracle_sample_tokens.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       P, P, ctypes.c_int64, ctypes.c_int64, P,
+                                       P, P, P, P, P, P, P]
+    L.oracle_token_logprobs_row.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, P, ctypes.c_int64, P, P, P]
+    L.oracle_sample_row_masked.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
+                                           P, ctypes.c_int64, P, P, P, P, P, P, P]
+    L.oracle_accept_windows.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+    L.oracle_draw_on_prefix.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_double, P]
+    for f in ("oracle_draw_on_prefix", "oracle_sample_row", "oracle_penalised_row",
+              "oracle_sample_tokens", "oracle_token_logprobs_row", "oracle_sample_row_masked",
+              "oracle_accept_windows"):
+        getattr(L, f).restype = ctypes.c_int
+    return L
 
 
 def lib():
     global _lib
+    if _lib_native is not None:
+        return _lib_native
     if _lib is None:
         if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
             build(force=True)
-        L = ctypes.CDLL(LIB)
-        P = ctypes.c_void_p
-        L.oracle_philox4x32_10.argtypes = [P, P, P]
-        L.oracle_philox4x32_10.restype = None
-        L.oracle_sample_row.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
-                                        P, P, P, P, P, P, P]
-        L.oracle_penalised_row.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64, P]
-        L.oracle_sample_tokens.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                           P, P, ctypes.c_int64, ctypes.c_int64, P,
-                                           P, P, P, P, P, P, P]
-        L.oracle_token_logprobs_row.argtypes = [P, ctypes.c_int64, ctypes.c_int32,
-                                                ctypes.c_int32, P, ctypes.c_int64, P, P, P]
-        L.oracle_sample_row_masked.argtypes = [P, ctypes.c_int64, P, P, ctypes.c_int64,
-                                               P, ctypes.c_int64, P, P, P, P, P, P, P]
-        L.oracle_accept_windows.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
-        L.oracle_draw_on_prefix.argtypes = [P, ctypes.c_int, ctypes.c_float, ctypes.c_double, P]
-        for f in ("oracle_draw_on_prefix", "oracle_sample_row", "oracle_penalised_row", "oracle_sample_tokens",
-                  "oracle_token_logprobs_row", "oracle_sample_row_masked",
-                  "oracle_accept_windows"):
-            getattr(L, f).restype = ctypes.c_int
-        _lib = L
+        _lib = _bind(ctypes.CDLL(LIB))
     return _lib
+
+
+def use_native_build(on: bool = True) -> None:
+    """Route every wrapper below through the -O3 -march=native build of the
+    same source (built on first use), or back to the -O2 build.  The calls
+    release the GIL, so host threads can run rows side by side."""
+    global _lib_native
+    if on and _lib_native is None:
+        _lib_native = _bind(ctypes.CDLL(build(force=True, native=True)))
+    elif not on:
+        _lib_native = None
 
 
 def _ptr(a):

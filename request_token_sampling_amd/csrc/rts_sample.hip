@@ -83,49 +83,53 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     constexpr int NQ = EPT / 4;
     __shared__ SampleSmem<EPT, LP> sm;
 
+    // Every argument the chunk's address depends on is read first and held
+    // by an empty asm statement, so the compiler issues these scalar loads
+    // together before the first branch instead of sinking each below the
+    // branch that needs it: the chunk's loads then go out one round trip
+    // after the start instead of three (measured on MI355X: one row read as
+    // two parameter rows 10.3 -> 9.8 us, 5 rows 12.9 -> 12.5 us).
+    const int early = a.early_xcds, cmaj = a.chunk_major, nch = a.nchunks, rows = a.rows;
+    const int V = a.V;
+    const float *const logits = a.logits;
+    const int64_t ld = a.ld;
+    asm volatile("" ::"s"(early), "s"(cmaj), "s"(nch), "s"(rows), "s"(V), "s"(logits), "s"(ld));
     if constexpr (LP) {
         // workgroups past the sampling grid renormalise over allowed lists
-        const int nsamp =
-            (int)grid_for(sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major), a.early_xcds);
+        const int nsamp = (int)grid_for(sample_work(rows, nch, early, cmaj), early);
         if ((int)blockIdx.x >= nsamp) {
             renorm_block(a, sm.s, sm.pen_cnt, (int)blockIdx.x - nsamp);
             return;
         }
     }
     const int tid = threadIdx.x;
-    const int lb = logical_block(a.early_xcds);
-    if (lb < 0 || lb >= sample_work(a.rows, a.nchunks, a.early_xcds, a.chunk_major)) return;
+    const int lb = logical_block(early);
+    if (lb < 0 || lb >= sample_work(rows, nch, early, cmaj)) return;
     int slot, chunk;
-    if (a.chunk_major) {
+    if (cmaj) {
         // Rows that share one logits row: the workgroups of one chunk for all
         // rows land on one XCD, so the chunk is fetched from HBM once and the
         // other rows read it from that XCD's L2.
-        const int P = xcds_used(a.early_xcds), x = lb % P, q = lb / P;
-        slot = q % a.rows;
-        chunk = (q / a.rows) * P + x;
-        if (chunk >= a.nchunks) return;  // padding workgroup
+        const int P = xcds_used(early), xx = lb % P, q = lb / P;
+        slot = q % rows;
+        chunk = (q / rows) * P + xx;
+        if (chunk >= nch) return;  // padding workgroup
     } else {
-        slot = lb / a.nchunks;
-        chunk = lb - slot * a.nchunks;
+        slot = lb / nch;
+        chunk = lb - slot * nch;
     }
+    const int base = chunk * CH;
+    const float *x = logits + (int64_t)slot * ld;
+    // The chunk's loads go out before the row's parameters are read.  Ids
+    // past V read as NaN: never selected.
+    float v[EPT];
+    load_chunk<EPT, VEC>(x, base, V, v);
     const SampleRow R = a.row[slot];
-    const int V = a.V;
     const int n_eff = (int)(R.pack & 0xFFFFu);
     const int k = (int)((R.pack >> 16) & 0x7Fu);
     const bool greedy = ((R.pack >> 24) & 1u) != 0u;
-    const int base = chunk * CH;
-    const float *x = a.logits + (int64_t)slot * a.ld;
-
-    // Each thread's first history id is loaded before the chunk: loads return
-    // in order, so one issued after the chunk's could only be used once the
-    // whole chunk had arrived, and the bitmap build below could not overlap
-    // the chunk's loads.  (The fused-logprob variant reads its chunk before
-    // the penalties and keeps the plain order.)
     const int32_t *h = a.history + R.hist_off;
     const int32_t h0 = (!LP && n_eff > 0 && tid < n_eff) ? h[tid] : -1;
-    // Then every load of the chunk.  Ids past V read as NaN: never selected.
-    float v[EPT];
-    load_chunk<EPT, VEC>(x, base, V, v);
     // A row renormalised over an allowed list: the workgroups of its first
     // eight chunks (one per XCD) touch every line of the list, so the row's
     // merging workgroup finds it in its XCD's L2.
