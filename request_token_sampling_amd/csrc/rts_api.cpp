@@ -35,21 +35,28 @@ int fail(int code, const char *fmt, ...)
 void clear_error() { g_last_error[0] = '\0'; }
 
 // Rows per launch and elements per thread.  A launch covers up to 64 rows;
-// each workgroup covers a chunk of 256 * ept elements.  The per-workgroup
-// selection cost is nearly independent of the chunk size while the row merge
-// grows with the number of chunks, so the chunk is the largest whose grid
-// still has >= 60 workgroups (measured on MI355X at V = 248,320: one row is
-// fastest at 4,096 elements per chunk, 5 and 40 rows at 8,192); the smallest
-// chunk is 1,024 elements.
+// each workgroup covers a chunk of 256 * ept elements.  A smaller chunk
+// shortens the per-workgroup selection (its ballot compaction takes one step
+// per element a thread holds) while the row merge grows with the chunks per
+// row, and a grid larger than the chip holds at once (five workgroups per CU)
+// runs in two rounds.  So the chunk is the smallest with at most 64 chunks
+// per row whose grid still fits one round; when none does, the largest
+// (8,192 elements).  Measured on MI355X at V = 248,320: one row read as two
+// parameter rows 10.0 -> 9.45 us and a 5-row window 12.4 -> 12.0 us at 4,096
+// elements against 8,192; 2,048 was slower for both (9.66, 12.0 at 4,096 and
+// 11.0 us at 1,024 for the former); 40 rows stay at 8,192.
+constexpr int64_t kMaxChunksPerRow = 64;
+constexpr int64_t kResidentWorkgroups = 5 * 256;
+
 int choose_ept(int64_t rows, int64_t V)
 {
-    static const int opts[4] = {32, 16, 8, 4};
+    static const int opts[4] = {4, 8, 16, 32};
     for (int i = 0; i < 4; ++i) {
         const int64_t ch = (int64_t)rts::kBlock * opts[i];
         const int64_t nch = (V + ch - 1) / ch;
-        if (rows * nch >= 60) return opts[i];
+        if (nch <= kMaxChunksPerRow && rows * nch <= kResidentWorkgroups) return opts[i];
     }
-    return 4;
+    return 32;
 }
 
 int64_t chunks_for(int64_t V, int ept)
