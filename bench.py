@@ -571,6 +571,12 @@ def _oracle_step(name):
     import oracle.oracle as O
     from request_token_sampling_amd import workloads as W
 
+    if name == "tiny":
+        w = W.tiny()
+        x = w["logits"]
+        jobs = [lambda r=r, p=p: O.sample_row(x[r], p)
+                for ps in (w["sampled"], w["greedy"]) for r, p in enumerate(ps)]
+        return jobs, x.shape[0], x.nbytes, "4 rows of V=1,024, sampled and greedy passes"
     if name == "single_stream":
         w = W.single_stream()
         x = w["logits"][0]
@@ -618,7 +624,7 @@ def cpu_baseline(reps=10):
     cores = host_threads()
     out = {}
     try:
-        for name in ("single_stream", "window", "batch", "stress"):
+        for name in ("tiny", "single_stream", "window", "batch", "stress"):
             jobs, rows, nbytes, what = _oracle_step(name)
             res = {"sample": what}
             for threads in (1, cores):

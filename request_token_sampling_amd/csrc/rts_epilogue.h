@@ -9,6 +9,46 @@ namespace rts {
 
 constexpr int kPackedWindow = 33;  // windows this long or shorter take window_step_packed
 
+// What the row's merging workgroup writes through, read from the kernel's
+// argument block in one place.  The compiler otherwise issues a scalar load
+// of each pointer next to its first store and waits for it there, so the
+// tail of every row paid about nine scalar round trips one after another;
+// read while the merge's loads are in flight and held in registers (the
+// empty asm makes each value opaque, so it is not re-read at its use), they
+// cost nothing on the tail.
+// (The pointers carry the global address space: made opaque, they would
+// otherwise lose it and every store would take the flat path.)
+#define RTS_GLOBAL __attribute__((address_space(1)))
+struct RowOut {
+    RTS_GLOBAL int32_t *token;
+    RTS_GLOBAL int32_t *counts;
+    RTS_GLOBAL int32_t *kept_ids;
+    RTS_GLOBAL float *kept_logits;
+    RTS_GLOBAL uint32_t *philox_x0;
+    RTS_GLOBAL uint64_t *counters;
+    int64_t counter_stride;
+    RTS_GLOBAL uint32_t *tickets;
+    RTS_GLOBAL const int32_t *draft;
+    RTS_GLOBAL int32_t *accepted;
+    RTS_GLOBAL uint32_t *wtickets;
+    int32_t window;
+};
+
+__device__ __forceinline__ RowOut row_out(const SampleArgs &a)
+{
+    RowOut o{(RTS_GLOBAL int32_t *)a.token,        (RTS_GLOBAL int32_t *)a.counts,
+             (RTS_GLOBAL int32_t *)a.kept_ids,     (RTS_GLOBAL float *)a.kept_logits,
+             (RTS_GLOBAL uint32_t *)a.philox_x0,   (RTS_GLOBAL uint64_t *)a.counters,
+             a.counter_stride,                     (RTS_GLOBAL uint32_t *)a.tickets,
+             (RTS_GLOBAL const int32_t *)a.draft,  (RTS_GLOBAL int32_t *)a.accepted,
+             (RTS_GLOBAL uint32_t *)a.wtickets,    a.window};
+    asm volatile("" : "+s"(o.token), "+s"(o.counts), "+s"(o.kept_ids), "+s"(o.kept_logits),
+                      "+s"(o.philox_x0), "+s"(o.counters), "+s"(o.counter_stride));
+    asm volatile("" : "+s"(o.tickets), "+s"(o.draft), "+s"(o.accepted), "+s"(o.wtickets),
+                      "+s"(o.window));
+    return o;
+}
+
 // llama.cpp-style penalty of an id seen c > 0 times in the window: the repeat
 // penalty divides a positive logit and multiplies a non-positive one, the
 // frequency term scales with the count and the presence term is charged once.
@@ -36,13 +76,13 @@ __device__ __forceinline__ float penalize(float v, uint32_t c, float rep, float 
 // read) to the window's 64-bit word with one device-scope atomic, so the
 // last arrival reads every row's outcome from the value the atomic returns;
 // no token is published and nothing else is read.
-__device__ __forceinline__ void window_step_packed(const SampleArgs &a, int slot, int32_t tok,
+__device__ __forceinline__ void window_step_packed(const RowOut &a, int slot, int32_t tok,
                                                    int32_t draft)
 {
     if (lane_id() != 0) return;
     const int w = slot / a.window, r = slot - w * a.window;
     const uint64_t add = (1ull << 32) | ((r < a.window - 1 && tok == draft) ? (1ull << r) : 0ull);
-    uint64_t *word = reinterpret_cast<uint64_t *>(&a.wtickets[w * kTicketStride]);
+    RTS_GLOBAL uint64_t *word = reinterpret_cast<RTS_GLOBAL uint64_t *>(&a.wtickets[w * kTicketStride]);
     const uint64_t old =
         __hip_atomic_fetch_add(word, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if ((old >> 32) != (uint64_t)(a.window - 1)) return;
@@ -50,12 +90,12 @@ __device__ __forceinline__ void window_step_packed(const SampleArgs &a, int slot
     const uint32_t span = rows >= 32u ? 0xFFFFFFFFu : ((1u << rows) - 1u);
     const uint32_t miss = ~(uint32_t)(old + add) & span;
     a.accepted[w] = miss ? __ffs(miss) : a.window;
-    publish_u64(word, 0ull);  // ready for the next launch on this workspace
+    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
 }
 
 // Longer windows: the row's token is published, then a ticket, and the last
 // row reads every row's token back.
-__device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32_t tok)
+__device__ __forceinline__ void window_step(const RowOut &a, int slot, int32_t tok)
 {
     const int lane = lane_id();
     const int w = slot / a.window;
@@ -70,7 +110,8 @@ __device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32
     const int r0 = w * a.window;
     bool miss = false;
     if (lane < a.window - 1) {
-        const int32_t t = (r0 + lane == slot) ? tok : read_published_i32(&a.token[r0 + lane]);
+        const int32_t t = (r0 + lane == slot) ? tok
+                          : __hip_atomic_load(&a.token[r0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         miss = t != a.draft[r0 + lane];
     }
     const uint64_t b = __ballot(miss);
@@ -82,7 +123,7 @@ __device__ __forceinline__ void window_step(const SampleArgs &a, int slot, int32
 
 // The cuts and the draw, run by wave 0 of the row's last workgroup on the
 // merged kept sequence sm.sel[0..k).  Leaves the sampled token in sm.flag.
-__device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
+__device__ __forceinline__ void epilogue(const RowOut &a, const SampleRow &R, SelectSmem &sm,
                                          int slot, int k, bool greedy, uint64_t ctr, uint32_t x0)
 {
     const int lane = lane_id();
@@ -141,7 +182,8 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     const int32_t tok = lane_i32(id, pick);
     if (lane == 0) {
         sm.flag = (uint32_t)tok;
-        if (a.window > kPackedWindow) publish_i32(&a.token[slot], tok);  // read by the window's last row
+        if (a.window > kPackedWindow)  // read by the window's last row
+            __hip_atomic_store(&a.token[slot], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else a.token[slot] = tok;
         if (a.counts) {
             a.counts[3 * (int64_t)slot + 0] = k;
@@ -154,6 +196,13 @@ __device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R
     }
     if (a.window > kPackedWindow) window_step(a, slot, tok);
     else if (a.window > 0) window_step_packed(a, slot, tok, draft);
+}
+
+// The same for callers that have not read the outputs ahead.
+__device__ __forceinline__ void epilogue(const SampleArgs &a, const SampleRow &R, SelectSmem &sm,
+                                         int slot, int k, bool greedy, uint64_t ctr, uint32_t x0)
+{
+    epilogue(row_out(a), R, sm, slot, k, greedy, ctr, x0);
 }
 
 }  // namespace rts

@@ -267,7 +267,9 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // looks the drawn token up in them.
     const bool renorm = LP && (R.pack & kPackRenorm) != 0u;
     int32_t al[kRenormPerThread];
+    RowOut ro;
     list_topk(sm.s, list, a.nchunks, k, [&]() {
+        ro = row_out(a);
         if (renorm) {
             const int32_t *ids = a.allowed + R.allowed_off;
 #pragma unroll
@@ -281,7 +283,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
 
     const int wave = tid >> 6, lane = lane_id();
     if (!LP) {
-        if (wave == 0) epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
+        if (wave == 0) epilogue(ro, R, sm.s, slot, k, greedy, ctr, x0);
         return;
     }
 
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
         const uint64_t kept = lane < k ? sm.s.sel[lane] : 0ull;
         const float xr = kept ? x[key_index(kept)] : 0.0f;
         if (renorm && lane == 0) enc = read_published_u64(lpa_w);  // done already?
-        epilogue(a, R, sm.s, slot, k, greedy, ctr, x0);
+        epilogue(ro, R, sm.s, slot, k, greedy, ctr, x0);
         const int32_t t = (int32_t)sm.s.flag;  // the sampled token, left by the epilogue
         if (renorm && lane == 0 && enc == 0ull)
             enc = __hip_atomic_exchange(lpa_w, kSamplerTag | (uint32_t)t, __ATOMIC_RELAXED,

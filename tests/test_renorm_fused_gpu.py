@@ -188,6 +188,40 @@ def test_masked_rows_take_the_separate_pass():
     check(x, params, 20, lists, "masked + renorm", mask_lists=masks)
 
 
+def test_masked_rows_past_the_bitmap_limit():
+    """Rows with a candidate mask renormalise their lists after the launch; at
+    V = 1,100,003 (past 2^19, where no vocabulary bitmap fits in LDS) that pass
+    takes the hash-set kernel, which handles 64 rows a launch: 66 restricted
+    rows make two launches.  Lists of up to 2,048 ids with repeats and foreign
+    ids, a list whose members are all -inf, an empty list, and top_n 20 and 0."""
+    rng = np.random.default_rng(43)
+    Vx, B = 1_100_003, 66
+    x = rng.normal(0, 3, (B, Vx)).astype(np.float32)
+    params = [W.row_params() if r % 11 == 0 else
+              sampled(top_k=int(rng.integers(1, 65)), counter=r, top_p=0.9)
+              for r in range(B)]
+    masks, lists = [], []
+    for r in range(B):
+        m = rng.choice(Vx, 3000, replace=False).astype(np.int32)
+        masks.append(m)
+        c = r % 4
+        if c == 0:    # members from the mask and outside it, repeats, foreign ids
+            a = np.concatenate([m[:700], rng.integers(0, Vx, 600), m[:40], [-1, Vx, Vx + 9]])
+        elif c == 1:  # the longest list renormalised in one pass
+            a = rng.integers(0, Vx, 2048)
+        elif c == 2:
+            a = rng.choice(Vx, 900, replace=False)
+        else:
+            a = np.zeros(0, np.int64) if r % 8 == 3 else m[::3]
+        lists.append(np.asarray(a, np.int32))
+    # row 5: every member of its list is -inf (each gets -log of the member count)
+    lists[5] = rng.choice(Vx, 400, replace=False).astype(np.int32)
+    x[5, lists[5]] = -np.inf
+    check(x, params, 20, lists, "masked renorm V past 2^19", mask_lists=masks)
+    check(x[:4], params[:4], 0, lists[:4], "masked renorm V past 2^19, top_n 0",
+          mask_lists=masks[:4])
+
+
 def test_small_rows_many_launches():
     """70 rows of 1,024 ids (two launches, one chunk per row): the sampling
     side often finishes before the renormalising workgroup."""
