@@ -483,8 +483,11 @@ def summarize_counters(paths, workload, cmd):
     ratio("valu_active_per_wave_cycle", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES")
     ratio("salu_per_valu_inst", "SQ_INSTS_SALU", "SQ_INSTS_VALU")
     ratio("lds_per_valu_inst", "SQ_INSTS_LDS", "SQ_INSTS_VALU")
+    ratio("wait_any_per_wave_cycle_all", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+    ratio("lds_bank_conflict_per_lds_active", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS")
     if "SQ_WAVES" in med and med["SQ_WAVES"] > 0:
-        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES"):
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_SMEM",
+                  "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_WAVE_CYCLES"):
             if k in med:
                 lines.append(f"{k}_per_wave = {med[k] / med['SQ_WAVES']:.1f}")
     lines.append(f"source_sha256 = {kernel_source_hash()}")
