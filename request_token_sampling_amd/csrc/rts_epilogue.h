@@ -160,20 +160,27 @@ __device__ __forceinline__ void epilogue(const RowOut &a, const SampleRow &R, Se
         if (!head_masked && m > 1 && !same_w) w = (lane < m) ? exp(dy / (double)R.temperature) : 0.0;
         // top_p: shortest prefix of the min_p survivors whose fp64 softmax
         // mass reaches top_p; a masked head (-inf) keeps one candidate.
+        // Both inclusive scans run before the top_p cut is known, so their
+        // chains overlap: lane j of a DPP scan only adds lanes below it, so
+        // the tempered sums of the lanes below the cut are the same whether
+        // the lanes past it hold their weights or zeros; with a temperature
+        // of 1 the draw reuses the untempered scan.
+        double Sd = 0.0, Sw = 0.0;
+        if (use_top_p) Sd = wave_scan_f64(lane < m ? d : 0.0);
+        if (!head_masked && m > 1 && !same_w) Sw = wave_scan_f64(w);  // w is 0 past m
         n = m;
         if (head_masked) {
             n = 1;
         } else if (use_top_p) {
-            const double S = wave_scan_f64(lane < m ? d : 0.0);
-            const double Z = lane_f64(S, m - 1);
-            const uint64_t b = __ballot(lane < m && S / Z >= (double)R.top_p);
+            const double Z = lane_f64(Sd, m - 1);
+            const uint64_t b = __ballot(lane < m && Sd / Z >= (double)R.top_p);
             n = b ? __ffsll((unsigned long long)b) : m;
         }
         // temperature, then the draw: u = x0 / 2^32 against the tempered CDF.
         const double u = (double)x0 * (1.0 / 4294967296.0);
         pick = n - 1;
         if (n > 1) {
-            const double S = wave_scan_f64(lane < n ? (same_w ? d : w) : 0.0);
+            const double S = same_w ? Sd : Sw;
             const double Z = lane_f64(S, n - 1);
             const uint64_t b = __ballot(lane < n - 1 && S / Z > u);
             if (b) pick = __ffsll((unsigned long long)b) - 1;
