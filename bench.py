@@ -366,7 +366,8 @@ def measure(wl, steps, warmup, warm=True, alt=True):
     eager = time_eager(wl, steps, warmup)
     graph = time_graph(wl, steps)
     warm = time_graph(wl, steps, warm=True) if warm else None
-    kern = kernel_durations(wl, min(steps, 500))
+    # at least 300 launches whatever K is: a short run's first launches run slow
+    kern = kernel_durations(wl, max(300, min(steps, 500)))
     alt = time_alt_graph(wl, steps) if (alt and wl.alt_calls) else None
     return dict(graph_wall=graph, warm_wall=warm, eager_wall=eager, kern_ms=kern,
                 floor=read_floor(wl), alt=alt)

@@ -395,16 +395,6 @@ __device__ __forceinline__ void publish_u64(uint64_t *p, uint64_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish_i32(int32_t *p, int32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ int32_t read_published_i32(const int32_t *p)
-{
-    return __hip_atomic_load(const_cast<int32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ uint64_t read_published_u64(const uint64_t *p)
 {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
