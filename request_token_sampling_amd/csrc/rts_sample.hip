@@ -128,6 +128,11 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     const int n_eff = (int)(R.pack & 0xFFFFu);
     const int k = (int)((R.pack >> 16) & 0x7Fu);
     const bool greedy = ((R.pack >> 24) & 1u) != 0u;
+    // Each thread's first history id: loads return in order, so it arrives
+    // with the chunk's last load and the bitmap build below waits for the
+    // chunk.  Loading it first would need the row's parameters first, one
+    // more scalar round trip before the chunk's loads, which measured slower
+    // on every workload, penalised ones included.
     const int32_t *h = a.history + R.hist_off;
     const int32_t h0 = (!LP && n_eff > 0 && tid < n_eff) ? h[tid] : -1;
     // A row renormalised over an allowed list: the workgroups of its first
