@@ -177,6 +177,30 @@ def test_long_rows_many_chunks(B, Vx):
         check(x, params, tag=f"long rows V={Vx} k={ks}")
 
 
+@pytest.mark.parametrize("B", [20, 21, 64])
+def test_chunk_size_boundaries_full_vocab(B):
+    """At V = 248,320 a launch of up to 20 rows takes 4,096-element chunks
+    and from 21 rows 8,192 (the chunk is the smallest with at most 64 chunks
+    per row whose grid fits one resident round); 64 rows of 8,192-element
+    chunks make 1,984 workgroups, more than fit at once.  Penalised rows
+    sharing history rows of different lengths, mixed top_k."""
+    rng = np.random.default_rng(700 + B)
+    H, ldh = 3, 256
+    hist = rng.integers(0, V, (H, ldh)).astype(np.int32)
+    hist_len = np.array([256, 100, 0], np.int32)
+    # history ids lifted into the head, so the penalties decide kept sets
+    x = W.boost_history(rng.normal(0, 3, (B, V)).astype(np.float32), hist[:2].ravel(), 9.0)
+    params = []
+    for r in range(B):
+        kw = dict(top_k=int(rng.integers(1, 65)), counter=r, seed=r + 5, top_p=0.9, min_p=0.02,
+                  temperature=float(np.float32(rng.uniform(0.3, 1.5))))
+        if r % 3 != 2:
+            kw.update(penalty_repeat=1.1, penalty_freq=0.5, penalty_present=0.5,
+                      penalty_last_n=64 + 32 * (r % 4), history_row=r % H)
+        params.append(sampled(**kw))
+    check(x, params, hist, hist_len, tag=f"{B} rows at full V")
+
+
 def test_integer_grid_ties_full_vocab():
     rng = np.random.default_rng(8)
     x = rng.integers(-20, 21, (6, V)).astype(np.float32)
