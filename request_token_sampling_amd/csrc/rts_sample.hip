@@ -135,12 +135,6 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     // on every workload, penalised ones included.
     const int32_t *h = a.history + R.hist_off;
     const int32_t h0 = (!LP && n_eff > 0 && tid < n_eff) ? h[tid] : -1;
-    // A row renormalised over an allowed list: the workgroups of its first
-    // eight chunks (one per XCD) touch every line of the list, so the row's
-    // merging workgroup finds it in its XCD's L2.
-    int32_t pf = 0;
-    if (LP && (R.pack & kPackRenorm) != 0u && chunk < 8 && tid * 32 < R.allowed_cnt)
-        pf = a.allowed[R.allowed_off + tid * 32];
 
     // Raw-logit logprobs in the same pass (page "#3200 ...", "Approach": the
     // reported distribution is taken before penalties and temperature): the
@@ -158,9 +152,6 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerSimd) void sample_kernel(const 
     uint64_t *raw_out = LP ? a.raw_keys + (int64_t)slot * a.raw_stride + (int64_t)chunk * K : nullptr;
     bool raw_done = false;
     if (LP) {
-        // keeps the prefetch load (its value is unused); the wait for it is
-        // the wait for the chunk's own loads, issued before it
-        asm volatile("" ::"v"(pf));
         const float2 lms = lane_max_sum<EPT>(v, [&]() {
             // ids below V among the lane's groups of four
             int c = 0;
